@@ -1,0 +1,257 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle (the modules
+``oracle.rope64``, ``oracle.attn64``) disagrees with a closed form, an
+invariant of the mathematics, a library routine or the independent scalar
+twin ``oracle.brute``. ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle (on the
+CPU) and checks that some pin fails for each.
+
+The definition pinned: 3D rotary encoding over (t, h, w) bands of the head
+dimension, adjacent rotary pairs, angle ``p_a * theta**(-2i/D_a)``,
+counter-clockwise turn; dense softmax attention over every key with no mask
+(MiniMax-H3 deep-dive page, attention paragraph after the DiT configuration
+table; StreamRender-H3 page, streaming-context section).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import attn64, brute, rope64
+
+AX128 = (32, 48, 48)
+THETA = 10000.0
+
+
+def _rng(tag):
+    return np.random.default_rng(np.random.SeedSequence([20261203, tag]))
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    ref = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    assert err <= rtol * ref, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {ref:.3e}"
+
+
+def _tiny_case(tag, d, axis_dims, heads, seg_rows, nq, prompt=0):
+    rng = _rng(tag)
+    q = rng.standard_normal((nq, heads, d))
+    q_pos = rng.random((nq, 3)) * 30.0
+    segs = []
+    if prompt:
+        segs.append((rng.standard_normal((prompt, heads, d)), rng.standard_normal((prompt, heads, d)), None))
+    for r in seg_rows:
+        segs.append((rng.standard_normal((r, heads, d)), rng.standard_normal((r, heads, d)),
+                     rng.random((r, 3)) * 30.0))
+    return q, q_pos, segs
+
+
+def pin_brute_force():
+    """Vectorised oracle == scalar-loop twin on tiny inputs, rel <= 1e-12."""
+    cases = [
+        (1, 2, (2, 0, 0), 1, [3], 2, 0),
+        (2, 4, (2, 2, 0), 2, [2, 3], 3, 2),
+        (3, 8, (2, 2, 4), 1, [4, 1], 2, 1),
+        (4, 64, (16, 24, 24), 2, [5, 4], 3, 3),
+        (5, 128, AX128, 1, [3, 2], 2, 2),
+    ]
+    for tag, d, ax, heads, rows, nq, prompt in cases:
+        q, qp, segs = _tiny_case(tag, d, ax, heads, rows, nq, prompt)
+        scale = 1.0 / math.sqrt(d)
+        got = attn64.chunk_attention(q, qp, segs, ax, THETA, scale)
+        ref = brute.chunk_attention(q.tolist(), qp.tolist(),
+                                    [(k.tolist(), v.tolist(), None if p is None else p.tolist()) for k, v, p in segs],
+                                    ax, THETA, scale)
+        _close(got, ref, 1e-12, f"brute force d={d}")
+
+
+def pin_rotation_closed_form():
+    """rotate(e_2p) = cos(phi) e_2p + sin(phi) e_2p+1, phi = p_a theta^(-2i/D_a).
+
+    Checked for every rotary pair of the 32/48/48 split of d = 128; also
+    rotate(e_2p+1) = -sin(phi) e_2p + cos(phi) e_2p+1.
+    """
+    d = 128
+    pos = np.array([[3.0, 17.5, 40.25]])
+    base = 0
+    for a, width in enumerate(AX128):
+        for i in range(width // 2):
+            p = base // 2 + i
+            phi = pos[0, a] * THETA ** (-2.0 * i / width)
+            for comp, expect in ((0, {2 * p: math.cos(phi), 2 * p + 1: math.sin(phi)}),
+                                 (1, {2 * p: -math.sin(phi), 2 * p + 1: math.cos(phi)})):
+                x = np.zeros((1, 1, d))
+                x[0, 0, 2 * p + comp] = 1.0
+                y = rope64.rotate(x, rope64.angles(pos, AX128, THETA))[0, 0]
+                want = np.zeros(d)
+                for idx, val in expect.items():
+                    want[idx] = val
+                _close(y, want, 1e-13, f"rotation closed form band {a} pair {i}")
+        base += width
+
+
+def pin_rotation_group():
+    """Rotation is orthogonal, R(0) = I and R(a) R(b) = R(a + b)."""
+    rng = _rng(11)
+    x = rng.standard_normal((5, 2, 128))
+    pa = rng.random((5, 3)) * 50
+    pb = rng.random((5, 3)) * 50
+    ra = rope64.rotate(x, rope64.angles(pa, AX128, THETA))
+    _close(np.linalg.norm(ra, axis=-1), np.linalg.norm(x, axis=-1), 1e-13, "norm preserved")
+    _close(rope64.rotate(x, rope64.angles(np.zeros((5, 3)), AX128, THETA)), x, 1e-15, "R(0) = I")
+    rab = rope64.rotate(ra, rope64.angles(pb, AX128, THETA))
+    _close(rab, rope64.rotate(x, rope64.angles(pa + pb, AX128, THETA)), 1e-11, "R(a)R(b) = R(a+b)")
+
+
+def pin_single_pair_scores():
+    """Score of one-hot q, k in pair i of band a = scale cos((pq_a - pk_a) f_i).
+
+    Read back through the full attention with two keys (k1 one-hot, k2 = 0,
+    v1 = e_0, v2 = 0): o_0 = sigmoid(s1), so s1 = logit(o_0).
+    """
+    d, heads = 128, 1
+    scale = 0.7
+    pq = np.array([[5.0, 11.0, 2.0]])
+    pk = np.array([[2.0, 4.5, 9.0], [0.0, 0.0, 0.0]])
+    base = 0
+    for a, width in enumerate(AX128):
+        for i in (0, 1, width // 4, width // 2 - 1):
+            p = base // 2 + i
+            q = np.zeros((1, heads, d))
+            q[0, 0, 2 * p] = 1.0
+            k = np.zeros((2, heads, d))
+            k[0, 0, 2 * p] = 1.0
+            v = np.zeros((2, heads, d))
+            v[0, 0, 0] = 1.0
+            o = attn64.chunk_attention(q, pq, [(k, v, pk)], AX128, THETA, scale)[0, 0, 0]
+            s1 = math.log(o / (1.0 - o))
+            want = scale * math.cos((pq[0, a] - pk[0, a]) * THETA ** (-2.0 * i / width))
+            assert abs(s1 - want) <= 1e-10, f"band {a} pair {i}: score {s1} != {want}"
+        base += width
+
+
+def pin_softmax_rows():
+    """Softmax rows are non-negative and sum to 1 (|sum - 1| <= 1e-12)."""
+    rng = _rng(21)
+    s = rng.standard_normal((7, 300)) * 6.0
+    p = attn64.softmax_rows(s)
+    assert np.all(p >= 0.0)
+    _close(p.sum(axis=-1), np.ones(7), 1e-12, "softmax row sums")
+    # order-preserving and shift-invariant
+    _close(attn64.softmax_rows(s + 3.5), p, 1e-12, "softmax shift invariance")
+    assert np.all(np.argsort(p[0]) == np.argsort(s[0]))
+
+
+def pin_constant_v():
+    """All value rows equal c  =>  every output row equals c."""
+    q, qp, segs = _tiny_case(31, 128, AX128, 2, [40, 25], 9, prompt=6)
+    c = _rng(32).standard_normal((2, 128))
+    segs = [(k, np.broadcast_to(c, v.shape).copy(), p) for k, v, p in segs]
+    o = attn64.chunk_attention(q, qp, segs, AX128, THETA, 1 / math.sqrt(128))
+    _close(o, np.broadcast_to(c, o.shape), 1e-12, "constant V")
+
+
+def pin_joint_permutation():
+    """Permuting key/value rows with their positions leaves the output unchanged.
+
+    Also moves rows between segments (segment boundaries carry no meaning).
+    """
+    q, qp, segs = _tiny_case(41, 128, AX128, 2, [30, 20], 6, prompt=5)
+    scale = 1 / math.sqrt(128)
+    o = attn64.chunk_attention(q, qp, segs, AX128, THETA, scale)
+    (kp, vp, _), (k1, v1, p1), (k2, v2, p2) = segs
+    k = np.concatenate([k1, k2])
+    v = np.concatenate([v1, v2])
+    p = np.concatenate([p1, p2])
+    perm = _rng(42).permutation(k.shape[0])
+    cut = 17
+    segs2 = [(k[perm[:cut]], v[perm[:cut]], p[perm[:cut]]),
+             (kp[::-1], vp[::-1], None),
+             (k[perm[cut:]], v[perm[cut:]], p[perm[cut:]])]
+    o2 = attn64.chunk_attention(q, qp, segs2, AX128, THETA, scale)
+    _close(o2, o, 1e-12, "joint permutation")
+
+
+def pin_zero_angle_is_sdpa():
+    """All positions 0 (and no rotary at all) == torch SDPA in float64 on CPU."""
+    rng = _rng(51)
+    nq, nk, heads, d = 13, 37, 3, 128
+    q = rng.standard_normal((nq, heads, d))
+    k = rng.standard_normal((nk, heads, d))
+    v = rng.standard_normal((nk, heads, d))
+    scale = 0.37
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    ref = ref.permute(1, 0, 2).numpy()
+    zero = attn64.chunk_attention(q, np.zeros((nq, 3)), [(k[:20], v[:20], np.zeros((20, 3))),
+                                                         (k[20:], v[20:], np.zeros((nk - 20, 3)))],
+                                  AX128, THETA, scale)
+    _close(zero, ref, 1e-12, "zero angle vs SDPA")
+    none = attn64.chunk_attention(q, None, [(k, v, None)], AX128, THETA, scale)
+    _close(none, ref, 1e-12, "no rotary vs SDPA")
+
+
+def pin_two_keys():
+    """o = sigmoid(s1 - s2) v1 + sigmoid(s2 - s1) v2 with s = scale <q, k>."""
+    rng = _rng(61)
+    d = 128
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((2, 1, d))
+    v = rng.standard_normal((2, 1, d))
+    scale = 0.21
+    o = attn64.chunk_attention(q, None, [(k[:1], v[:1], None), (k[1:], v[1:], None)], AX128, THETA, scale)
+    s1 = scale * math.fsum(q[0, 0] * k[0, 0])
+    s2 = scale * math.fsum(q[0, 0] * k[1, 0])
+    w1 = 1.0 / (1.0 + math.exp(s2 - s1))
+    w2 = 1.0 / (1.0 + math.exp(s1 - s2))
+    _close(o[0, 0], w1 * v[0, 0] + w2 * v[1, 0], 1e-13, "two keys")
+
+
+def pin_degenerate():
+    """scale = 0 gives the mean of the values; a single key returns its value."""
+    q, qp, segs = _tiny_case(71, 128, AX128, 2, [11, 6], 4, prompt=3)
+    o = attn64.chunk_attention(q, qp, segs, AX128, THETA, 0.0)
+    vall = np.concatenate([v for _, v, _ in segs])
+    _close(o, np.broadcast_to(vall.mean(axis=0), o.shape), 1e-13, "scale 0 -> mean")
+    k1, v1, p1 = segs[1]
+    o1 = attn64.chunk_attention(q, qp, [(k1[:1], v1[:1], p1[:1])], AX128, THETA, 0.3)
+    _close(o1, np.broadcast_to(v1[0], o1.shape), 1e-15, "single key")
+
+
+def pin_translation():
+    """Shifting every Q and K position on one axis leaves the output unchanged
+    when every segment is rotary, and changes it when a non-rotary prompt
+    segment is present (relative-position property of rotary encoding)."""
+    q, qp, segs = _tiny_case(81, 128, AX128, 2, [24, 19], 7)
+    scale = 1 / math.sqrt(128)
+    o = attn64.chunk_attention(q, qp, segs, AX128, THETA, scale)
+    for axis, delta in ((0, 100.0), (1, 7.25), (2, -31.0)):
+        sh = np.zeros(3)
+        sh[axis] = delta
+        o2 = attn64.chunk_attention(q, qp + sh, [(k, v, p + sh) for k, v, p in segs], AX128, THETA, scale)
+        _close(o2, o, 1e-10, f"translation invariance axis {axis}")
+    q, qp, segs = _tiny_case(82, 128, AX128, 2, [24, 19], 7, prompt=8)
+    o = attn64.chunk_attention(q, qp, segs, AX128, THETA, scale)
+    sh = np.array([100.0, 0.0, 0.0])
+    o2 = attn64.chunk_attention(q, qp + sh, [(k, v, None if p is None else p + sh) for k, v, p in segs],
+                                AX128, THETA, scale)
+    assert np.max(np.abs(o2 - o)) > 1e-4, "a prompt segment must break translation invariance"
+
+
+def pin_row_selection():
+    """Selecting query rows gives exactly those rows of the full output."""
+    q, qp, segs = _tiny_case(91, 128, AX128, 2, [33, 8], 20, prompt=4)
+    scale = 1 / math.sqrt(128)
+    full = attn64.chunk_attention(q, qp, segs, AX128, THETA, scale, block=7)
+    rows = np.array([19, 0, 7, 13])
+    part = attn64.chunk_attention(q, qp, segs, AX128, THETA, scale, rows=rows)
+    _close(part, full[rows], 1e-14, "row selection")
+
+
+ALL_PINS = [pin_brute_force, pin_rotation_closed_form, pin_rotation_group, pin_single_pair_scores,
+            pin_softmax_rows, pin_constant_v, pin_joint_permutation, pin_zero_angle_is_sdpa,
+            pin_two_keys, pin_degenerate, pin_translation, pin_row_selection]

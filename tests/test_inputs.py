@@ -1,0 +1,67 @@
+"""Seeded workload generator: shapes, positions, rounding and determinism."""
+
+import json
+import os
+
+import numpy as np
+import torch
+
+from streaming_video_diffusion_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "workload_shapes.json")
+
+
+def test_shapes_match_fixture():
+    fx = json.load(open(GOLDEN))
+    assert set(I.CONFIGS) == {k for k in fx if not k.startswith("_")}
+    for name, make in I.CONFIGS.items():
+        w, want = make(), fx[name]
+        assert (w.heads, w.head_dim, w.nq, w.nk) == (want["heads"], want["head_dim"], want["nq"], want["nk"])
+        assert [[s.name, s.rows] for s in w.segments] == want["segments"]
+        assert w.calls == want.get("calls", 1)
+        assert sum(a for a in w.axis_dims) == w.head_dim
+        for s in w.segments:
+            assert (s.pos is None) == (s.name == "prompt")
+            if s.pos is not None:
+                assert s.pos.shape == (s.rows, 3) and s.pos.dtype == np.float32
+
+
+def test_positions_layout():
+    w = I.full_1344x768()
+    ref = w.segments[1].pos
+    assert ref[0].tolist() == [0, 0, 0] and ref[1].tolist() == [0, 0, 1]
+    assert ref[84].tolist() == [0, 1, 0] and ref[-1].tolist() == [0, 47, 83]
+    cur = w.segments[-1].pos
+    assert np.array_equal(cur, w.q_pos)
+    assert cur[0, 0] == 4 and cur[-1, 0] == 6
+    h = I.hier_1344x768()
+    pool4, pool2 = h.segments[2].pos, h.segments[3].pos
+    assert pool4[0].tolist() == [1, 1.5, 1.5] and pool4[-1].tolist() == [3, 45.5, 81.5]
+    assert pool2[0].tolist() == [4, 0.5, 0.5] and pool2[-1].tolist() == [6, 46.5, 82.5]
+    va = I.video_audio_1344x768()
+    aud = va.q_pos[-40:]
+    assert np.all(aud[:, 1:] == 0)
+    np.testing.assert_array_equal(aud[:, 0], np.float32(7 + 0.15 * np.arange(40)))
+    assert va.q_pos[24191].tolist() == [12, 47, 83]
+
+
+def test_round_bf16_matches_torch():
+    x = np.random.default_rng(5).standard_normal(100000).astype(np.float32) * 3
+    x[:4] = [1.00390625, 1.01171875, -2.00781250, 0.0]   # exact ties either way
+    ours = I.round_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_draws_are_seeded_and_distinct():
+    w = I.lowres_bf16()
+    a, b = w.q(), w.q()
+    np.testing.assert_array_equal(a, b)
+    k0, v0 = w.kv(0)
+    assert not np.array_equal(k0, v0)
+    assert np.array_equal(I.round_bf16(a), a)
+    va = I.video_audio_1344x768()
+    assert va.calls == 2
+    ss = [np.random.SeedSequence([I.ENTROPY, 5, c, 0]).generate_state(2).tolist() for c in (0, 1)]
+    assert ss[0] != ss[1]
+    assert abs(float(a.std()) - 1.0) < 0.02

@@ -1,0 +1,113 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check a pin catches each.
+
+This shows the pins are strong enough: a dropped term, a wrong sign, a wrong
+index or a transposed operand anywhere in the oracle fails at least one of
+them. The oracle itself is restored after every case by ``monkeypatch``.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import attn64, rope64
+
+
+def _rotate_with(fn):
+    def rotate(x, phi):
+        x = np.asarray(x, dtype=np.float64)
+        squeeze = x.ndim == 2
+        if squeeze:
+            x = x[:, None, :]
+        n, _, d = x.shape
+        phi = np.asarray(phi, dtype=np.float64).reshape(n, d // 2)
+        out = fn(x, np.cos(phi)[:, None, :], np.sin(phi)[:, None, :])
+        return out[:, 0, :] if squeeze else out
+    return rotate
+
+
+def _adjacent(form):
+    def fn(x, c, s):
+        out = np.empty_like(x)
+        xe, xo = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2], out[..., 1::2] = form(xe, xo, c, s)
+        return out
+    return fn
+
+
+def _half_split(x, c, s):
+    half = x.shape[-1] // 2
+    out = np.empty_like(x)
+    a, b = x[..., :half], x[..., half:]
+    out[..., :half] = a * c - b * s
+    out[..., half:] = a * s + b * c
+    return out
+
+
+def _freq_with(expo):
+    def pair_axis_and_freq(axis_dims, theta):
+        axis, freq = [], []
+        for a, width in enumerate(axis_dims):
+            for i in range(int(width) // 2):
+                axis.append(a)
+                freq.append(float(theta) ** expo(i, int(width), sum(axis_dims)))
+        return np.asarray(axis), np.asarray(freq)
+    return pair_axis_and_freq
+
+
+def _angles_reversed_axes(pos, axis_dims, theta):
+    pos = np.asarray(pos, dtype=np.float64).reshape(-1, 3)
+    axis, freq = rope64.pair_axis_and_freq(axis_dims, theta)
+    return pos[:, 2 - axis] * freq[None, :]
+
+
+def _attention_with(weighted, softmax_axis=-1, use_scale=True):
+    def attention(q, k, v, scale, block=512):
+        q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+        out = np.empty(q.shape, dtype=np.float64)
+        for h in range(q.shape[1]):
+            s = (scale if use_scale else 1.0) * (q[:, h, :] @ k[:, h, :].T)
+            m = np.max(s, axis=softmax_axis, keepdims=True)
+            e = np.exp(s - m)
+            p = e / np.sum(e, axis=softmax_axis, keepdims=True)
+            out[:, h, :] = p @ weighted(k, v)[:, h, :]
+        return out
+    return attention
+
+
+def _rotated_keys_unrotated(segments, axis_dims, theta):
+    ks = [np.asarray(k, dtype=np.float64) for k, _, _ in segments]
+    vs = [np.asarray(v, dtype=np.float64) for _, v, _ in segments]
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+MUTATIONS = {
+    "clockwise_turn": [(rope64, "rotate", _rotate_with(_adjacent(
+        lambda xe, xo, c, s: (xe * c + xo * s, -xe * s + xo * c))))],
+    "cos_sin_swapped": [(rope64, "rotate", _rotate_with(_adjacent(
+        lambda xe, xo, c, s: (xe * s - xo * c, xe * c + xo * s))))],
+    "half_split_pairs": [(rope64, "rotate", _rotate_with(_half_split))],
+    "second_term_dropped": [(rope64, "rotate", _rotate_with(_adjacent(
+        lambda xe, xo, c, s: (xe * c, xe * s + xo * c))))],
+    "freq_missing_factor_2": [(rope64, "pair_axis_and_freq", _freq_with(lambda i, w, d: -1.0 * i / w))],
+    "freq_over_head_dim": [(rope64, "pair_axis_and_freq", _freq_with(lambda i, w, d: -2.0 * i / d))],
+    "freq_index_off_by_one": [(rope64, "pair_axis_and_freq", _freq_with(lambda i, w, d: -2.0 * (i + 1) / w))],
+    "axes_reversed": [(rope64, "angles", _angles_reversed_axes)],
+    "softmax_unnormalised": [(attn64, "softmax_rows", lambda s: np.exp(np.asarray(s) - np.max(s, axis=-1, keepdims=True)))],
+    "softmax_over_queries": [(attn64, "attention", _attention_with(lambda k, v: v, softmax_axis=0))],
+    "weights_times_keys": [(attn64, "attention", _attention_with(lambda k, v: k))],
+    "scale_dropped": [(attn64, "attention", _attention_with(lambda k, v: v, use_scale=False))],
+    "keys_not_rotated": [(attn64, "rotated_keys", _rotated_keys_unrotated)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    for module, attr, repl in MUTATIONS[name]:
+        monkeypatch.setattr(module, attr, repl)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, ZeroDivisionError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name!r} passed every pin"
