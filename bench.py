@@ -1,0 +1,174 @@
+"""Benchmark: streaming-chunk attention at 1344x768 on one MI355X.
+
+A step is one chunk through the whole hot path: rotary tables of the chunk's
+position template, in-place pack of the dynamic K/V region (history and the
+current chunk; the static prompt/reference prefix is packed once, before
+timing), and the forward pass. Inputs are resident in HBM before timing.
+
+Prints ONE JSON line. ``value`` is attention TFLOP/s over the whole step
+(4*Nq*Nk*d*H flops per chunk / step time); ``ms_per_step`` is ms per chunk.
+``roofline`` prices the forward kernel (the dominant kernel) from HIP events
+around each of its launches in the timed region; ``cpu_baseline`` times the
+fp64 oracle on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + ms/chunk at 1344x768 (12096 q x 28480 kv, 40 heads)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (published)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="full_1344x768")
+    p.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(w, rows_n):
+    """Time the fp64 oracle on a bounded sample: rotation of every key of the
+    call plus ``rows_n`` query rows (all heads); extrapolate linearly in rows
+    (rows are independent)."""
+    import numpy as np
+    from oracle import attn64
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = w.q(0)
+    segs = [(*w.kv(i, 0), s.pos) for i, s in enumerate(w.segments)]
+    rows = np.random.default_rng(7).choice(w.nq, size=min(rows_n, w.nq), replace=False)
+    t0 = time.perf_counter()
+    kr, vr = attn64.rotated_keys(segs, w.axis_dims, w.theta)
+    t1 = time.perf_counter()
+    from oracle import rope64
+    qs = rope64.rotate(q[rows], rope64.angles(w.q_pos[rows], w.axis_dims, w.theta))
+    attn64.attention(qs, kr, vr, w.scale)
+    t2 = time.perf_counter()
+    per_call = (t1 - t0) + (t2 - t1) * w.nq / len(rows)
+    ms_chunk = per_call * w.calls * 1e3
+    return {
+        "value": w.flops_per_call() * w.calls / (ms_chunk * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {w.nq} query rows x {w.heads} heads plus rotation of all {w.nk} keys, "
+                   f"one call, fp64 numpy; extrapolated linearly to {w.nq} rows x {w.calls} call(s)"),
+        "ms_per_chunk": ms_chunk,
+        "measured_s": t2 - t0,
+        "host_cpus": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from streaming_video_diffusion_amd import inputs as I
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+
+    w = I.CONFIGS[args.workload]()
+    calls = [ChunkAttention(w, call=c, device="cuda:0") for c in range(w.calls)]
+    stream = torch.cuda.current_stream()
+    for ca in calls:
+        ca.pack_static(stream)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for ca in calls:
+            ca.step(stream)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    fwd_ev, pack_ev = [], []
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        for ca in calls:
+            p0, p1, f1 = ev(), ev(), ev()
+            p0.record(stream)
+            ca._tables(True, stream)
+            ca._pack(True, stream)
+            p1.record(stream)
+            ca.forward(stream)
+            f1.record(stream)
+            pack_ev.append((p0, p1))
+            fwd_ev.append((p1, f1))
+    end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in fwd_ev]
+    pack_ms = [a.elapsed_time(b) for a, b in pack_ev]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    flops_chunk = w.flops_per_call() * w.calls
+    flops_launch = w.flops_per_call()
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    achieved = flops_launch / (fwd_avg * 1e-3) / 1e12
+    fwd_sorted = sorted(fwd_ms)
+
+    out = {
+        "metric": METRIC,
+        "value": flops_chunk / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1), bf16-rounded; no real latents or weights)",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "nq": w.nq, "nk": w.nk, "heads": w.heads, "head_dim": w.head_dim, "calls": w.calls,
+            "segments": [[s.name, s.rows, "dynamic" if s.dynamic else "static"] for s in w.segments],
+            "step": "rope tables (dynamic template) + in-place pack of dynamic K/V + forward",
+            "flops_per_chunk": flops_chunk,
+            "entropy": I.ENTROPY,
+        },
+        "forward_ms_avg": fwd_avg,
+        "forward_ms_median": fwd_sorted[len(fwd_sorted) // 2],
+        "forward_tflops": achieved,
+        "pack_tables_ms_avg": sum(pack_ms) / len(pack_ms),
+        "roofline": {
+            "bound": "mfma" if bf16 else "alu",
+            "kernel": "fwd_bf16_kernel<128>" if bf16 else "fwd_f32_kernel",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

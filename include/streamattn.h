@@ -1,0 +1,213 @@
+/*
+ * libstreamattn -- streaming-chunk DiT self-attention on MI355X (gfx950).
+ *
+ * The operation: the current chunk's video-latent queries, carrying 3D
+ * (time, height, width) rotary position encoding, attend with dense softmax
+ * attention and no mask to one key/value set concatenated from a persistent
+ * style-prompt segment, the session reference frame, clean history (older
+ * history optionally at coarser, pooled resolution) and the current chunk.
+ *
+ *   - dense softmax attention with 3D MM-RoPE and QK-norm, head dim 128:
+ *     MiniMax-H3 deep-dive page, DiT configuration table and the attention
+ *     paragraph after it;
+ *   - bidirectional window, moving part attends to the whole window, prefix
+ *     (conditions, reference, sink) key/values computed once per denoising
+ *     step and reused: StreamRender-H3 page, streaming-context section;
+ *   - one cache bank per denoising step, per-layer persistent K/V buffers in
+ *     the layout the attention kernel reads with only the dynamic region
+ *     rewritten in place, lengths/offsets reused with no host-device sync:
+ *     StreamRender-H3 page, inference-acceleration section;
+ *   - persistent style-prompt key/values in every self-attention layer,
+ *     chunk-autoregressive history with progressively lower-resolution older
+ *     tiers: AlayaRenderer-Flash page, key contributions and technical details.
+ *
+ * Conventions for every call:
+ *   - All pointers to tensors are device pointers (HIP global memory) owned by
+ *     the caller. The library allocates no memory and keeps no pointer after
+ *     a call returns (kernels already enqueued still read/write them).
+ *   - Every call validates its arguments on the host before enqueueing any
+ *     work. On an invalid argument it returns a negative sa_status, enqueues
+ *     nothing and records a message for sa_last_error(). No C++ exception
+ *     crosses this interface.
+ *   - Work is enqueued on the caller's stream; no call synchronises the
+ *     device or the stream, none uses the null stream unless the caller passes
+ *     it, and none allocates, so calls may be captured into a HIP graph.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Calls are thread-safe. The only library state is the per-thread message
+ *     behind sa_last_error().
+ *   - Element strides are in elements, not bytes. The last (head_dim)
+ *     dimension of every tensor is contiguous. Base pointers and every row /
+ *     head start must be 16-byte aligned.
+ */
+#ifndef STREAMATTN_H
+#define STREAMATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+/* Packed context capacity (rows) must be a multiple of this. */
+#define SA_ROW_ALIGN 16
+/* Most segments one sa_pack_context call accepts. */
+#define SA_MAX_SEGMENTS 16
+
+typedef int32_t sa_status;
+#define SA_OK 0
+#define SA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SA_ERR_SHAPE (-2)       /* a size, stride, axis split or row range is invalid */
+#define SA_ERR_DTYPE (-3)       /* unknown or mismatched element type */
+#define SA_ERR_ALIGN (-4)       /* a pointer or stride breaks 16-byte alignment */
+#define SA_ERR_CAPACITY (-5)    /* rows exceed the packed capacity, or capacity not a multiple of SA_ROW_ALIGN */
+#define SA_ERR_UNSUPPORTED (-6) /* valid but not implemented (e.g. head_dim other than 64 / 128) */
+#define SA_ERR_HIP (-7)         /* a HIP launch failed; sa_last_error() holds HIP's message */
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/*
+ * Rotary specification. The head dimension is cut into three consecutive
+ * bands of even widths axis_dims = (D_t, D_h, D_w), summing to head_dim. Pair
+ * i of band a covers dimensions (o_a + 2i, o_a + 2i + 1) and turns by
+ * phi = p_a * theta^(-2i / D_a), where p_a is the token's coordinate on that
+ * axis: (x, y) -> (x cos phi - y sin phi, x sin phi + y cos phi).
+ * (The pages name 3D MM-RoPE over time, height and width -- MiniMax-H3
+ * deep-dive page, components table and DiT paragraph -- but not its split,
+ * frequencies or pair layout; this is the plain reading adopted.)
+ */
+typedef struct {
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t axis_dims[3]; /* (D_t, D_h, D_w): even, >= 0, sum == head_dim */
+    double theta;         /* rotary base, > 0 (10000 in the shipped workloads) */
+} sa_rope_spec;
+
+/*
+ * sa_make_rope_tables -- build the rotary table of n tokens.
+ *
+ * pos_thw: device float32 [n][3], (t, h, w) coordinate of each token.
+ * table:   device float32 [n][head_dim/2][2], written with (cos phi, sin phi)
+ *          of every rotary pair; angles are formed in float64 and rounded once.
+ * n may be 0 (nothing is enqueued). A table is built once per position
+ * template and reused across layers, heads and denoising steps (the window
+ * reuses one position template after its first chunk: StreamRender-H3 page,
+ * streaming-context section).
+ * Errors: SA_ERR_NULL (spec, or pos/table with n > 0), SA_ERR_SHAPE (axis
+ * split, theta, n < 0), SA_ERR_UNSUPPORTED (head_dim), SA_ERR_ALIGN, SA_ERR_HIP.
+ */
+sa_status sa_make_rope_tables(const sa_rope_spec *spec, const float *pos_thw, int64_t n, float *table,
+                              hipStream_t stream);
+
+/*
+ * One source segment of the key/value context (style prompt, reference frame,
+ * a history tier, or the current chunk).
+ * Element (row r, head h, dim c) of K is at k[r*k_row_stride + h*k_head_stride + c],
+ * likewise for V; K and V have the context's dtype.
+ */
+typedef struct {
+    const void *k;
+    const void *v;
+    int64_t rows;          /* >= 0; 0 is legal (e.g. no history yet) */
+    int64_t k_row_stride;  /* elements */
+    int64_t k_head_stride; /* elements */
+    int64_t v_row_stride;  /* elements */
+    int64_t v_head_stride; /* elements */
+    const float *rope;     /* device [rows][head_dim/2][2] table from sa_make_rope_tables,
+                              or NULL: keys used unrotated (the persistent prompt K/V) */
+    int64_t dst_row;       /* first packed row this segment fills */
+} sa_segment;
+
+/*
+ * A packed key/value context: the persistent per-layer buffers the forward
+ * kernel reads (one context per layer and per denoising-step bank).
+ *
+ * Layout of k_packed / v_packed (capacity_rows = C, head_dim = d, heads = H):
+ *   SA_BF16: K  bfloat16 [H][C][d], each row already rotated by its segment's
+ *               table and rounded once to bfloat16 (round to nearest even);
+ *            V  bfloat16 [H][d][C] (key index minor). Within every aligned
+ *               group of 16 rows, row 16g + j is stored at column
+ *               16g + perm(j), perm = (0 1 2 3 8 9 10 11 4 5 6 7 12 13 14 15)
+ *               (an involution: it swaps rows 4..7 with rows 8..11), so that a
+ *               matrix-core lane reads its 8 keys as one 16-byte vector.
+ *   SA_F32:  K  float32 [H][C][d] rotated; V float32 [H][C][d].
+ * rows (Nk) is the number of valid packed rows; the forward pass attends to
+ * rows [0, rows) and never reads past them (up to the next multiple of 16).
+ */
+typedef struct {
+    int32_t heads;         /* >= 1 */
+    int32_t head_dim;      /* 64 or 128 */
+    sa_dtype dtype;        /* element type of K, V (and of Q in sa_forward) */
+    int64_t capacity_rows; /* allocated rows, a multiple of SA_ROW_ALIGN */
+    int64_t rows;          /* valid rows Nk, 1 <= rows <= capacity_rows for sa_forward */
+    void *k_packed;        /* device, sa_packed_bytes() bytes */
+    void *v_packed;        /* device, sa_packed_bytes() bytes */
+} sa_context;
+
+/*
+ * sa_packed_bytes -- size in bytes of each of k_packed and v_packed.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
+ * SA_ERR_CAPACITY (capacity_rows not a multiple of SA_ROW_ALIGN).
+ */
+sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64_t capacity_rows,
+                          size_t *bytes_each);
+
+/*
+ * sa_pack_context -- gather segments into the packed K/V buffers.
+ *
+ * Each segment's rows are written to packed rows [dst_row, dst_row + rows),
+ * keys rotated by the segment's table (fused into the load: no separate RoPE
+ * pass), values copied (bf16: transposed as documented above). Packed rows
+ * not covered by a segment of this call are left untouched, so the static
+ * prefix (prompt, reference) can be packed once per bank and the dynamic
+ * region (history, current chunk) rewritten in place every chunk.
+ * Segment row ranges must lie inside [0, ctx->rows) and must not overlap.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (n_segs outside [0, SA_MAX_SEGMENTS],
+ * ranges, strides), SA_ERR_CAPACITY, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
+ * SA_ERR_ALIGN, SA_ERR_HIP.
+ */
+sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t n_segs, hipStream_t stream);
+
+/*
+ * sa_forward -- attention of nq query rows over the packed context.
+ *
+ * q:      device [nq][heads][head_dim] of ctx->dtype, element (r, h, c) at
+ *         q[r*q_row_stride + h*q_head_stride + c].
+ * q_rope: device [nq][head_dim/2][2] table, or NULL for unrotated queries.
+ *         The rotation is fused into the query load (float32 math, one
+ *         rounding to bfloat16 on the SA_BF16 path).
+ * softmax_scale: multiplies <q, k> before the softmax (usually 1/sqrt(d)).
+ * out:    device [nq][heads][head_dim] of out_dtype (SA_BF16 or SA_F32),
+ *         element (r, h, c) at out[r*o_row_stride + h*o_head_stride + c].
+ *
+ * out[r][h] = sum_j softmax_j(softmax_scale * <R(pq_r) q_rh, K'_jh>) V_jh over
+ * all packed rows j < ctx->rows, with no mask (the moving part of the window
+ * attends to the whole window: StreamRender-H3 page, streaming-context
+ * section). SA_BF16: bf16 matrix-core products with float32 accumulation and
+ * float32 online softmax; SA_F32: float32 throughout.
+ * nq == 0 enqueues nothing. out must not overlap q or the packed buffers.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_CAPACITY (ctx->rows outside
+ * [1, capacity]), SA_ERR_DTYPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_HIP.
+ */
+sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                     int64_t q_head_stride, const float *q_rope, float softmax_scale, void *out,
+                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *sa_status_string(sa_status status);
+
+/* Detail of the calling thread's most recent failure ("" if none). The pointer
+ * stays valid until that thread's next libstreamattn call. */
+const char *sa_last_error(void);
+
+/* SA_ABI_VERSION of the loaded library. */
+int32_t sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMATTN_H */

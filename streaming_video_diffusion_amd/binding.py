@@ -1,0 +1,187 @@
+"""Thin ctypes binding of libstreamattn (argument marshalling only).
+
+The three calls keep the C names: ``sa_make_rope_tables``,
+``sa_pack_context`` and ``sa_forward``. They take torch tensors for device
+memory and enqueue on the current torch stream (or a given one); all work
+runs in the library's HIP kernels. There is no fallback: if the shared
+library is missing, the first call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamattn.so")
+
+SA_OK = 0
+SA_F32 = 0
+SA_BF16 = 1
+SA_ROW_ALIGN = 16
+SA_MAX_SEGMENTS = 16
+
+_DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
+_TORCH = {SA_F32: torch.float32, SA_BF16: torch.bfloat16}
+
+
+class SaError(RuntimeError):
+    """A libstreamattn call returned a negative status."""
+
+    def __init__(self, call, status, message):
+        self.status = status
+        self.message = message
+        super().__init__(f"{call} failed: {_status_name(status)} ({status}): {message}")
+
+
+class RopeSpec(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("axis_dims", ctypes.c_int32 * 3), ("theta", ctypes.c_double)]
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("k_row_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("v_row_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+                ("rope", ctypes.c_void_p), ("dst_row", ctypes.c_int64)]
+
+
+class Context(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("capacity_rows", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("k_packed", ctypes.c_void_p), ("v_packed", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libstreamattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m streaming_video_diffusion_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.sa_make_rope_tables.argtypes = [ctypes.POINTER(RopeSpec), vp, i64, vp, vp]
+        L.sa_make_rope_tables.restype = i32
+        L.sa_packed_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.sa_packed_bytes.restype = i32
+        L.sa_pack_context.argtypes = [ctypes.POINTER(Context), ctypes.POINTER(Segment), i32, vp]
+        L.sa_pack_context.restype = i32
+        L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.c_float, vp, i32,
+                                 i64, i64, vp]
+        L.sa_forward.restype = i32
+        L.sa_status_string.argtypes = [i32]
+        L.sa_status_string.restype = ctypes.c_char_p
+        L.sa_last_error.argtypes = []
+        L.sa_last_error.restype = ctypes.c_char_p
+        L.sa_abi_version.argtypes = []
+        L.sa_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _status_name(status):
+    try:
+        return lib().sa_status_string(status).decode()
+    except Exception:  # pragma: no cover - only when the library cannot load
+        return "?"
+
+
+def _check(call, status):
+    if status != SA_OK:
+        raise SaError(call, status, lib().sa_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows_heads(t, name):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [rows][heads][head_dim] with a contiguous last dim")
+    return t.stride(0), t.stride(1)
+
+
+def abi_version():
+    return lib().sa_abi_version()
+
+
+def packed_bytes(heads, head_dim, dtype, capacity_rows):
+    n = ctypes.c_size_t()
+    _check("sa_packed_bytes", lib().sa_packed_bytes(heads, head_dim, _DTYPES.get(dtype, dtype), capacity_rows,
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def padded_rows(rows):
+    """Smallest legal capacity (multiple of SA_ROW_ALIGN) holding ``rows``."""
+    return (rows + SA_ROW_ALIGN - 1) // SA_ROW_ALIGN * SA_ROW_ALIGN
+
+
+def sa_make_rope_tables(pos, head_dim, axis_dims, theta, table=None, stream=None):
+    """Rotary table [n][head_dim/2][2] (cos, sin) of positions ``pos`` [n][3] f32."""
+    n = pos.shape[0]
+    if table is None:
+        table = torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device=pos.device)
+    spec = RopeSpec(head_dim, (ctypes.c_int32 * 3)(*axis_dims), float(theta))
+    _check("sa_make_rope_tables", lib().sa_make_rope_tables(ctypes.byref(spec), _ptr(pos), n, _ptr(table),
+                                                            _stream(stream)))
+    return table
+
+
+class PackedContext:
+    """Persistent packed K/V buffers of one layer / denoising-step bank."""
+
+    def __init__(self, heads, head_dim, dtype, capacity_rows, device="cuda"):
+        cap = padded_rows(capacity_rows)
+        n = packed_bytes(heads, head_dim, dtype, cap)
+        elem = 2 if dtype == torch.bfloat16 else 4
+        self.k_packed = torch.empty(n // elem, dtype=dtype, device=device)
+        self.v_packed = torch.empty(n // elem, dtype=dtype, device=device)
+        self.heads, self.head_dim, self.dtype = heads, head_dim, dtype
+        self.capacity_rows = cap
+        self.rows = 0
+
+    def struct(self):
+        return Context(self.heads, self.head_dim, _DTYPES[self.dtype], self.capacity_rows, self.rows,
+                       self.k_packed.data_ptr(), self.v_packed.data_ptr())
+
+
+def make_segment(k, v, dst_row, rope=None):
+    """C segment descriptor for K/V views [rows][heads][head_dim] starting at packed row dst_row."""
+    krs, khs = _rows_heads(k, "k")
+    vrs, vhs = _rows_heads(v, "v")
+    if k.shape[0] != v.shape[0]:
+        raise ValueError("k and v must have the same number of rows")
+    return Segment(k.data_ptr(), v.data_ptr(), k.shape[0], krs, khs, vrs, vhs,
+                   None if rope is None else rope.data_ptr(), dst_row)
+
+
+def sa_pack_context(ctx, segments, stream=None):
+    """Pack ``segments`` (list of (k, v, dst_row, rope_or_None)) into ``ctx``."""
+    segs = [make_segment(k, v, dst, rope) for k, v, dst, rope in segments]
+    arr = (Segment * max(1, len(segs)))(*segs)
+    c = ctx.struct()
+    _check("sa_pack_context", lib().sa_pack_context(ctypes.byref(c), arr, len(segs), _stream(stream)))
+
+
+def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None):
+    """Attention of ``q`` [Nq][heads][head_dim] over the packed context."""
+    qrs, qhs = _rows_heads(q, "q")
+    if softmax_scale is None:
+        softmax_scale = ctx.head_dim ** -0.5
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    ors, ohs = _rows_heads(out, "out")
+    c = ctx.struct()
+    _check("sa_forward", lib().sa_forward(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs, _ptr(q_rope),
+                                          float(softmax_scale), _ptr(out), _DTYPES[out.dtype], ors, ohs,
+                                          _stream(stream)))
+    return out

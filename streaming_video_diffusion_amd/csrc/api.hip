@@ -1,0 +1,245 @@
+// libstreamattn C ABI: argument validation and dispatch.
+//
+// Every entry point checks its arguments on the host before enqueueing any
+// kernel, returns a status instead of throwing, and leaves a per-thread
+// message for sa_last_error(). No call allocates, synchronises, or touches a
+// stream other than the caller's.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+sa_status fail(sa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sa_status hip_fail(hipError_t e, const char *what) {
+    return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+
+int64_t elem_bytes(sa_dtype t) { return t == SA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == SA_F32 || t == SA_BF16; }
+
+// Strides must keep every row / head start on a 16-byte boundary.
+bool stride_ok(int64_t stride, sa_dtype t) { return stride >= 0 && (stride * elem_bytes(t)) % 16 == 0; }
+
+sa_status check_context(const sa_context *ctx) {
+    if (!ctx) return fail(SA_ERR_NULL, "ctx is NULL");
+    if (!valid_dtype(ctx->dtype)) return fail(SA_ERR_DTYPE, "ctx->dtype %d is not SA_F32 or SA_BF16", (int)ctx->dtype);
+    if (ctx->heads < 1 || ctx->heads > 65535) return fail(SA_ERR_SHAPE, "ctx->heads %d outside [1, 65535]", ctx->heads);
+    if (!supported_dim(ctx->head_dim))
+        return fail(SA_ERR_UNSUPPORTED, "ctx->head_dim %d (supported: 64, 128)", ctx->head_dim);
+    if (ctx->capacity_rows < 0 || ctx->capacity_rows % SA_ROW_ALIGN != 0)
+        return fail(SA_ERR_CAPACITY, "ctx->capacity_rows %lld is not a non-negative multiple of %d",
+                    (long long)ctx->capacity_rows, SA_ROW_ALIGN);
+    if (ctx->capacity_rows > (int64_t(1) << 31))
+        return fail(SA_ERR_CAPACITY, "ctx->capacity_rows %lld above 2^31", (long long)ctx->capacity_rows);
+    if (ctx->rows < 0 || ctx->rows > ctx->capacity_rows)
+        return fail(SA_ERR_CAPACITY, "ctx->rows %lld outside [0, capacity_rows %lld]", (long long)ctx->rows,
+                    (long long)ctx->capacity_rows);
+    if (!ctx->k_packed || !ctx->v_packed) return fail(SA_ERR_NULL, "ctx->k_packed / v_packed is NULL");
+    if (!aligned(ctx->k_packed, 16) || !aligned(ctx->v_packed, 16))
+        return fail(SA_ERR_ALIGN, "packed buffers must be 16-byte aligned");
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char *sa_last_error(void) { return g_err; }
+
+const char *sa_status_string(sa_status st) {
+    switch (st) {
+        case SA_OK: return "SA_OK";
+        case SA_ERR_NULL: return "SA_ERR_NULL";
+        case SA_ERR_SHAPE: return "SA_ERR_SHAPE";
+        case SA_ERR_DTYPE: return "SA_ERR_DTYPE";
+        case SA_ERR_ALIGN: return "SA_ERR_ALIGN";
+        case SA_ERR_CAPACITY: return "SA_ERR_CAPACITY";
+        case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+        case SA_ERR_HIP: return "SA_ERR_HIP";
+        default: return "SA_ERR_UNKNOWN";
+    }
+}
+
+sa_status sa_make_rope_tables(const sa_rope_spec *spec, const float *pos_thw, int64_t n, float *table,
+                              hipStream_t stream) {
+    g_err[0] = 0;
+    if (!spec) return fail(SA_ERR_NULL, "spec is NULL");
+    if (!supported_dim(spec->head_dim))
+        return fail(SA_ERR_UNSUPPORTED, "spec->head_dim %d (supported: 64, 128)", spec->head_dim);
+    int sum = 0;
+    for (int a = 0; a < 3; ++a) {
+        const int w = spec->axis_dims[a];
+        if (w < 0 || w % 2) return fail(SA_ERR_SHAPE, "axis_dims[%d] = %d must be even and >= 0", a, w);
+        sum += w;
+    }
+    if (sum != spec->head_dim)
+        return fail(SA_ERR_SHAPE, "axis_dims sum %d != head_dim %d", sum, spec->head_dim);
+    if (!(spec->theta > 0.0) || !std::isfinite(spec->theta))
+        return fail(SA_ERR_SHAPE, "theta must be finite and > 0");
+    if (n < 0) return fail(SA_ERR_SHAPE, "n = %lld < 0", (long long)n);
+    if (n == 0) return SA_OK;
+    if (!pos_thw || !table) return fail(SA_ERR_NULL, "pos_thw / table is NULL");
+    if (!aligned(pos_thw, 4) || !aligned(table, 16))
+        return fail(SA_ERR_ALIGN, "pos_thw must be 4-byte and table 16-byte aligned");
+
+    sa::RopeTableArgs a{};
+    a.pos = pos_thw;
+    a.table = table;
+    a.n = n;
+    a.pairs = spec->head_dim / 2;
+    int p = 0;
+    for (int ax = 0; ax < 3; ++ax) {
+        const int w = spec->axis_dims[ax];
+        for (int i = 0; i < w / 2; ++i, ++p) {
+            a.axis[p] = (int8_t)ax;
+            a.inv_freq[p] = std::pow(spec->theta, -2.0 * i / w);
+        }
+    }
+    hipError_t e = sa::launch_rope_tables(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "rope table launch");
+    return SA_OK;
+}
+
+sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64_t capacity_rows,
+                          size_t *bytes_each) {
+    g_err[0] = 0;
+    if (!bytes_each) return fail(SA_ERR_NULL, "bytes_each is NULL");
+    if (!valid_dtype(dtype)) return fail(SA_ERR_DTYPE, "dtype %d is not SA_F32 or SA_BF16", (int)dtype);
+    if (heads < 1 || heads > 65535) return fail(SA_ERR_SHAPE, "heads %d outside [1, 65535]", heads);
+    if (!supported_dim(head_dim)) return fail(SA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (capacity_rows < 0 || capacity_rows % SA_ROW_ALIGN != 0 || capacity_rows > (int64_t(1) << 31))
+        return fail(SA_ERR_CAPACITY, "capacity_rows %lld is not a multiple of %d in [0, 2^31]",
+                    (long long)capacity_rows, SA_ROW_ALIGN);
+    *bytes_each = (size_t)heads * (size_t)capacity_rows * (size_t)head_dim * (size_t)elem_bytes(dtype);
+    return SA_OK;
+}
+
+sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t n_segs, hipStream_t stream) {
+    g_err[0] = 0;
+    sa_status st = check_context(ctx);
+    if (st != SA_OK) return st;
+    if (n_segs < 0 || n_segs > SA_MAX_SEGMENTS)
+        return fail(SA_ERR_SHAPE, "n_segs %d outside [0, %d]", n_segs, SA_MAX_SEGMENTS);
+    if (n_segs > 0 && !segs) return fail(SA_ERR_NULL, "segs is NULL");
+    const int64_t eb = elem_bytes(ctx->dtype);
+    const int64_t d = ctx->head_dim;
+
+    sa::PackArgs a{};
+    a.k_packed = ctx->k_packed;
+    a.v_packed = ctx->v_packed;
+    a.cap = ctx->capacity_rows;
+    a.heads = ctx->heads;
+    int64_t max_tiles = 0;
+    int used = 0;
+    for (int i = 0; i < n_segs; ++i) {
+        const sa_segment &s = segs[i];
+        if (s.rows < 0) return fail(SA_ERR_SHAPE, "segment %d: rows %lld < 0", i, (long long)s.rows);
+        if (s.dst_row < 0 || s.dst_row + s.rows > ctx->rows)
+            return fail(SA_ERR_SHAPE, "segment %d: rows [%lld, %lld) outside packed rows [0, %lld)", i,
+                        (long long)s.dst_row, (long long)(s.dst_row + s.rows), (long long)ctx->rows);
+        if (s.rows == 0) continue;
+        if (!s.k || !s.v) return fail(SA_ERR_NULL, "segment %d: k / v is NULL", i);
+        if (!aligned(s.k, 16) || !aligned(s.v, 16) || (s.rope && !aligned(s.rope, 16)))
+            return fail(SA_ERR_ALIGN, "segment %d: k, v and rope must be 16-byte aligned", i);
+        if (!stride_ok(s.k_row_stride, ctx->dtype) || !stride_ok(s.k_head_stride, ctx->dtype) ||
+            !stride_ok(s.v_row_stride, ctx->dtype) || !stride_ok(s.v_head_stride, ctx->dtype))
+            return fail(SA_ERR_ALIGN, "segment %d: strides must be >= 0 and multiples of %lld elements", i,
+                        (long long)(16 / eb));
+        if ((s.rows > 1 && s.k_row_stride < d) || (ctx->heads > 1 && s.k_head_stride < d) ||
+            (s.rows > 1 && s.v_row_stride < d) || (ctx->heads > 1 && s.v_head_stride < d))
+            return fail(SA_ERR_SHAPE, "segment %d: a stride is smaller than head_dim", i);
+        for (int j = 0; j < i; ++j) {
+            const sa_segment &o = segs[j];
+            if (o.rows > 0 && s.dst_row < o.dst_row + o.rows && o.dst_row < s.dst_row + s.rows)
+                return fail(SA_ERR_SHAPE, "segments %d and %d overlap in the packed rows", j, i);
+        }
+        sa::PackSeg &p = a.seg[used++];
+        p.k = s.k;
+        p.v = s.v;
+        p.rope = s.rope;
+        p.rows = s.rows;
+        p.k_rs = s.k_row_stride;
+        p.k_hs = s.k_head_stride;
+        p.v_rs = s.v_row_stride;
+        p.v_hs = s.v_head_stride;
+        p.dst_row = s.dst_row;
+        const int64_t tiles =
+            (s.dst_row + s.rows - 1) / sa::kPackTileRows - s.dst_row / sa::kPackTileRows + 1;
+        if (tiles > max_tiles) max_tiles = tiles;
+    }
+    a.n_segs = used;
+    hipError_t e = sa::launch_pack(a, ctx->head_dim, ctx->dtype, max_tiles, stream);
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    return SA_OK;
+}
+
+sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
+                     const float *q_rope, float softmax_scale, void *out, sa_dtype out_dtype, int64_t o_row_stride,
+                     int64_t o_head_stride, hipStream_t stream) {
+    g_err[0] = 0;
+    sa_status st = check_context(ctx);
+    if (st != SA_OK) return st;
+    if (ctx->rows < 1) return fail(SA_ERR_CAPACITY, "ctx->rows must be >= 1 for sa_forward");
+    if (!valid_dtype(out_dtype)) return fail(SA_ERR_DTYPE, "out_dtype %d is not SA_F32 or SA_BF16", (int)out_dtype);
+    if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
+    if (!std::isfinite(softmax_scale)) return fail(SA_ERR_SHAPE, "softmax_scale must be finite");
+    if (nq == 0) return SA_OK;
+    if (nq > (int64_t(1) << 31)) return fail(SA_ERR_SHAPE, "nq above 2^31");
+    if (!q || !out) return fail(SA_ERR_NULL, "q / out is NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || (q_rope && !aligned(q_rope, 16)))
+        return fail(SA_ERR_ALIGN, "q, out and q_rope must be 16-byte aligned");
+    const int64_t d = ctx->head_dim;
+    if (!stride_ok(q_row_stride, ctx->dtype) || !stride_ok(q_head_stride, ctx->dtype) ||
+        !stride_ok(o_row_stride, out_dtype) || !stride_ok(o_head_stride, out_dtype))
+        return fail(SA_ERR_ALIGN, "q / out strides must be >= 0 and keep rows 16-byte aligned");
+    if ((nq > 1 && (q_row_stride < d || o_row_stride < d)) ||
+        (ctx->heads > 1 && (q_head_stride < d || o_head_stride < d)))
+        return fail(SA_ERR_SHAPE, "a q / out stride is smaller than head_dim");
+
+    sa::FwdArgs a{};
+    a.q = q;
+    a.q_rope = q_rope;
+    a.k = ctx->k_packed;
+    a.v = ctx->v_packed;
+    a.out = out;
+    a.q_rs = q_row_stride;
+    a.q_hs = q_head_stride;
+    a.o_rs = o_row_stride;
+    a.o_hs = o_head_stride;
+    a.nq = nq;
+    a.nk = ctx->rows;
+    a.cap = ctx->capacity_rows;
+    a.heads = ctx->heads;
+    a.out_f32 = out_dtype == SA_F32;
+    a.scale = softmax_scale;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    const int64_t rows_per_wg = ctx->dtype == SA_BF16 ? 256 : 64;
+    const int64_t blocks = ((nq + rows_per_wg - 1) / rows_per_wg) * ctx->heads;
+    if (blocks > 0x7fffffff) return fail(SA_ERR_SHAPE, "nq x heads too large for one grid");
+    hipError_t e = ctx->dtype == SA_BF16 ? sa::launch_fwd_bf16(a, ctx->head_dim, stream)
+                                         : sa::launch_fwd_f32(a, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return SA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// Context pack: gather key/value segments into the persistent packed buffers.
+//
+// The pages keep per-layer K/V buffers in the layout the attention kernel
+// reads and rewrite only the dynamic region in place (StreamRender-H3 page,
+// inference-acceleration section), and fuse rotary encoding with the cache
+// write (same page, Fast Causal H3 VAE section). Here one workgroup owns one
+// 64-row tile of the packed row space for one head and one segment:
+//   * keys: 16-byte coalesced loads, rotation in float32 by the segment's
+//     table, one rounding to bfloat16, 16-byte stores into K [H][C][d];
+//   * values (bf16): staged through LDS and written transposed into
+//     V [H][d][C] with the 16-row group permutation the forward kernel's
+//     matrix-core operand wants, 128 contiguous bytes per 8 lanes;
+//   * values (f32): copied row-major.
+// Rows outside the segment are never written, so the static prefix survives
+// an in-place rewrite of the dynamic rows. This pass is HBM-bound: each
+// element is read once and written once.
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Stored column j (within a 16-row group) holds packed row perm(j) of the
+// group; perm swaps 4..7 with 8..11 and is its own inverse.
+__device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+struct TileRange {
+    int64_t tile_start, lo, hi;  // packed rows [lo, hi) of this tile belong to the segment
+};
+
+__device__ __forceinline__ bool tile_range(const PackSeg &s, int64_t tx, TileRange &r) {
+    if (s.rows <= 0) return false;
+    const int64_t t0 = s.dst_row / kPackTileRows;
+    const int64_t t1 = (s.dst_row + s.rows - 1) / kPackTileRows;
+    if (tx > t1 - t0) return false;
+    r.tile_start = (t0 + tx) * kPackTileRows;
+    r.lo = s.dst_row > r.tile_start ? s.dst_row : r.tile_start;
+    const int64_t end = s.dst_row + s.rows;
+    r.hi = end < r.tile_start + kPackTileRows ? end : r.tile_start + kPackTileRows;
+    return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
+    constexpr int CH = D / 8;              // 16-byte chunks per row
+    constexpr int RPP = kThreads / CH;     // rows per pass
+    constexpr int PITCH = D + 8;           // LDS row pitch (elements)
+    __shared__ __align__(16) bf16 sv[kPackTileRows * PITCH];
+
+    const PackSeg s = a.seg[blockIdx.z];
+    TileRange r;
+    if (!tile_range(s, blockIdx.x, r)) return;
+    const int h = blockIdx.y;
+    const int t = threadIdx.x;
+    const int chunk = t % CH;
+
+    bf16 *kp = reinterpret_cast<bf16 *>(a.k_packed) + ((int64_t)h * a.cap) * D;
+    bf16 *vp = reinterpret_cast<bf16 *>(a.v_packed) + ((int64_t)h * D) * a.cap;
+    const bf16 *ks = reinterpret_cast<const bf16 *>(s.k);
+    const bf16 *vs = reinterpret_cast<const bf16 *>(s.v);
+
+#pragma unroll
+    for (int p = 0; p < kPackTileRows / RPP; ++p) {
+        const int lr = t / CH + p * RPP;
+        const int64_t row = r.tile_start + lr;
+        if (row < r.lo || row >= r.hi) continue;
+        const int64_t sr = row - s.dst_row;
+        bf16x8 kv = *reinterpret_cast<const bf16x8 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 8);
+        if (s.rope) {
+            const f32x4 *tb = reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 4) * 2);
+            const f32x4 t0 = tb[0], t1 = tb[1];
+            const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)kv[e];
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                const float c = cs[2 * pr], sn = cs[2 * pr + 1];
+                const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+                kv[2 * pr] = (bf16)(x0 * c - x1 * sn);
+                kv[2 * pr + 1] = (bf16)(x0 * sn + x1 * c);
+            }
+        }
+        *reinterpret_cast<bf16x8 *>(kp + row * D + chunk * 8) = kv;
+        const bf16x8 vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
+        *reinterpret_cast<bf16x8 *>(sv + lr * PITCH + chunk * 8) = vv;
+    }
+    __syncthreads();
+
+    // Transposed value store: vector (dd, vc) covers stored columns 8vc..8vc+7
+    // of d-row dd in this tile.
+    constexpr int NV = D * (kPackTileRows / 8);
+#pragma unroll
+    for (int i = 0; i < NV / kThreads; ++i) {
+        const int vid = t + i * kThreads;
+        const int dd = vid / (kPackTileRows / 8);
+        const int vc = vid % (kPackTileRows / 8);
+        bf16 *dst = vp + (int64_t)dd * a.cap + r.tile_start + vc * 8;
+        int lrow[8];
+        bool all = true;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int col = vc * 8 + jj;
+            lrow[jj] = (col & ~15) + group_perm(col & 15);
+            const int64_t row = r.tile_start + lrow[jj];
+            all = all && row >= r.lo && row < r.hi;
+        }
+        if (all) {
+            bf16x8 o;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) o[jj] = sv[lrow[jj] * PITCH + dd];
+            *reinterpret_cast<bf16x8 *>(dst) = o;
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int64_t row = r.tile_start + lrow[jj];
+                if (row >= r.lo && row < r.hi) dst[jj] = sv[lrow[jj] * PITCH + dd];
+            }
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
+    constexpr int CH = D / 4;           // 16-byte chunks per row (4 floats, 2 pairs)
+    constexpr int RPP = kThreads / CH;  // rows per pass
+    const PackSeg s = a.seg[blockIdx.z];
+    TileRange r;
+    if (!tile_range(s, blockIdx.x, r)) return;
+    const int h = blockIdx.y;
+    const int t = threadIdx.x;
+    const int chunk = t % CH;
+    float *kp = reinterpret_cast<float *>(a.k_packed) + ((int64_t)h * a.cap) * D;
+    float *vp = reinterpret_cast<float *>(a.v_packed) + ((int64_t)h * a.cap) * D;
+    const float *ks = reinterpret_cast<const float *>(s.k);
+    const float *vs = reinterpret_cast<const float *>(s.v);
+#pragma unroll
+    for (int p = 0; p < kPackTileRows / RPP; ++p) {
+        const int64_t row = r.tile_start + t / CH + p * RPP;
+        if (row < r.lo || row >= r.hi) continue;
+        const int64_t sr = row - s.dst_row;
+        f32x4 kv = *reinterpret_cast<const f32x4 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 4);
+        if (s.rope) {
+            const f32x4 cs = *reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 2) * 2);
+            const f32x4 x = kv;
+            kv.x = x.x * cs.x - x.y * cs.y;
+            kv.y = x.x * cs.y + x.y * cs.x;
+            kv.z = x.z * cs.z - x.w * cs.w;
+            kv.w = x.z * cs.w + x.w * cs.z;
+        }
+        *reinterpret_cast<f32x4 *>(kp + row * D + chunk * 4) = kv;
+        *reinterpret_cast<f32x4 *>(vp + row * D + chunk * 4) =
+            *reinterpret_cast<const f32x4 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 4);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream) {
+    if (a.n_segs == 0 || max_tiles == 0) return hipSuccess;
+    const dim3 grid((unsigned)max_tiles, (unsigned)a.heads, (unsigned)a.n_segs);
+    if (dtype == SA_BF16) {
+        if (head_dim == 128)
+            hipLaunchKernelGGL(pack_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(pack_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (head_dim == 128)
+            hipLaunchKernelGGL(pack_f32_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(pack_f32_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sa

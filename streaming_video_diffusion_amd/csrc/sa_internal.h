@@ -1,0 +1,69 @@
+// Internal declarations shared by the libstreamattn translation units.
+// Not part of the public C ABI (include/streamattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "streamattn.h"
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxPairs = 64;  // head_dim / 2 for head_dim 128
+
+// --- rotary tables --------------------------------------------------------
+struct RopeTableArgs {
+    const float *pos;  // [n][3]
+    float *table;      // [n][pairs][2]
+    int64_t n;
+    int32_t pairs;
+    int8_t axis[kMaxPairs];     // axis (0 t, 1 h, 2 w) of each pair
+    double inv_freq[kMaxPairs]; // theta^(-2i/D_a) of each pair
+};
+hipError_t launch_rope_tables(const RopeTableArgs &a, hipStream_t stream);
+
+// --- context pack ---------------------------------------------------------
+struct PackSeg {
+    const void *k;
+    const void *v;
+    const float *rope;
+    int64_t rows, k_rs, k_hs, v_rs, v_hs, dst_row;
+};
+struct PackArgs {
+    void *k_packed;
+    void *v_packed;
+    int64_t cap;
+    int32_t heads;
+    int32_t n_segs;
+    PackSeg seg[SA_MAX_SEGMENTS];
+};
+constexpr int kPackTileRows = 64;  // packed rows per pack workgroup
+hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream);
+
+// --- forward --------------------------------------------------------------
+struct FwdArgs {
+    const void *q;
+    const float *q_rope;
+    const void *k;   // packed K
+    const void *v;   // packed V
+    void *out;
+    int64_t q_rs, q_hs, o_rs, o_hs;
+    int64_t nq, nk, cap;
+    int32_t heads;
+    int32_t out_f32;
+    float scale;       // softmax scale
+    float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t stream);
+
+}  // namespace sa

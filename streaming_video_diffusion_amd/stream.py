@@ -1,0 +1,104 @@
+"""One streaming chunk's attention through libstreamattn.
+
+A ``ChunkAttention`` owns the persistent packed K/V buffers of one layer and
+one denoising-step bank. The static prefix (style-prompt K/V and the session
+reference frame) is packed once; every chunk then rebuilds the rotary tables
+of its position template, rewrites the dynamic region (history tiers and the
+current chunk) in place and runs the forward pass. This is the sequence the
+pages describe: prefix K/V computed once per denoising step and reused, only
+recent history and the current chunk recomputed, one cache bank per step,
+persistent per-layer buffers updated in place (StreamRender-H3 page,
+streaming-context and inference-acceleration sections).
+
+Device memory comes from torch; every step of the computation runs in the
+library's HIP kernels.
+"""
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class ChunkAttention:
+    """Persistent context + inputs of one attention call of a workload.
+
+    ``workload`` is an ``inputs.Workload``; ``call`` selects the denoising
+    step (its own bank and its own seeded tensors).
+    """
+
+    def __init__(self, workload, call=0, device="cuda", out_dtype=None):
+        w = workload
+        self.w = w
+        self.call = call
+        self.device = device
+        self.dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.out_dtype = out_dtype or self.dtype
+        dev = torch.device(device)
+
+        def up(x):
+            return torch.from_numpy(x).to(dev).to(self.dtype)
+
+        self.q = up(w.q(call))
+        self.q_pos = torch.from_numpy(w.q_pos).to(dev) if w.q_pos is not None else None
+        self.q_table = (torch.empty((w.nq, w.head_dim // 2, 2), dtype=torch.float32, device=dev)
+                        if w.q_pos is not None else None)
+        self.segs = []
+        row = 0
+        for i, s in enumerate(w.segments):
+            k, v = w.kv(i, call)
+            shares_q = (s.pos is not None and w.q_pos is not None and s.pos.shape == w.q_pos.shape
+                        and np.array_equal(s.pos, w.q_pos))
+            pos = None
+            table = None
+            if s.pos is not None and not shares_q and s.rows > 0:
+                pos = torch.from_numpy(s.pos).to(dev)
+                table = torch.empty((s.rows, w.head_dim // 2, 2), dtype=torch.float32, device=dev)
+            self.segs.append(dict(name=s.name, k=up(k), v=up(v), pos=pos, table=table, dst=row,
+                                  dynamic=s.dynamic, rotary=s.pos is not None, shares_q=shares_q))
+            row += s.rows
+        self.ctx = B.PackedContext(w.heads, w.head_dim, self.dtype, w.nk, device=dev)
+        self.ctx.rows = w.nk
+        self.out = torch.empty((w.nq, w.heads, w.head_dim), dtype=self.out_dtype, device=dev)
+
+    def _tables(self, dynamic, stream):
+        w = self.w
+        if dynamic and self.q_table is not None:
+            B.sa_make_rope_tables(self.q_pos, w.head_dim, w.axis_dims, w.theta, table=self.q_table, stream=stream)
+        for s in self.segs:
+            if s["dynamic"] == dynamic and s["table"] is not None:
+                B.sa_make_rope_tables(s["pos"], w.head_dim, w.axis_dims, w.theta, table=s["table"], stream=stream)
+
+    def _pack(self, dynamic, stream):
+        segs = []
+        for s in self.segs:
+            if s["dynamic"] != dynamic:
+                continue
+            rope = self.q_table if s["shares_q"] else (s["table"] if s["rotary"] else None)
+            segs.append((s["k"], s["v"], s["dst"], rope))
+        B.sa_pack_context(self.ctx, segs, stream=stream)
+
+    def pack_static(self, stream=None):
+        """Build the static prefix's tables and pack it (once per bank)."""
+        self._tables(False, stream)
+        self._pack(False, stream)
+
+    def step(self, stream=None, rebuild_tables=True):
+        """One chunk: rotary tables of the template, dynamic pack, forward."""
+        if rebuild_tables:
+            self._tables(True, stream)
+        self._pack(True, stream)
+        return self.forward(stream)
+
+    def forward(self, stream=None):
+        B.sa_forward(self.ctx, self.q, self.q_table, self.w.scale, out=self.out, stream=stream)
+        return self.out
+
+    def host_inputs(self):
+        """The exact host values fed to the device (for the oracle)."""
+        w = self.w
+        segs = []
+        for i, s in enumerate(w.segments):
+            k, v = w.kv(i, self.call)
+            segs.append((k, v, s.pos))
+        return w.q(self.call), w.q_pos, segs

@@ -1,0 +1,177 @@
+"""C ABI contract checks that need no GPU.
+
+The library must load and export every function ``include/streamattn.h``
+declares, and every argument error must be reported synchronously, before
+any HIP call (these calls return before touching the device).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from streaming_video_diffusion_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamattn.h")
+
+ERR = dict(NULL=-1, SHAPE=-2, DTYPE=-3, ALIGN=-4, CAPACITY=-5, UNSUPPORTED=-6, HIP=-7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from streaming_video_diffusion_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"sa_make_rope_tables", "sa_pack_context", "sa_forward"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in streamattn.h but not exported"
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SA_ROW_ALIGN (\d+)", text).group(1)) == B.SA_ROW_ALIGN
+    assert int(re.search(r"#define SA_MAX_SEGMENTS (\d+)", text).group(1)) == B.SA_MAX_SEGMENTS
+    for name, val in ERR.items():
+        assert re.search(rf"#define SA_ERR_{name} \({val}\)", text), name
+    assert ctypes.sizeof(B.RopeSpec) == 24
+    assert ctypes.sizeof(B.Segment) == 72
+    assert ctypes.sizeof(B.Context) == 48
+
+
+def test_version_and_status_strings(L):
+    assert L.sa_abi_version() == 1
+    assert L.sa_status_string(0) == b"SA_OK"
+    for name, val in ERR.items():
+        assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
+    assert L.sa_status_string(-99) == b"SA_ERR_UNKNOWN"
+
+
+def spec(d=128, ax=(32, 48, 48), theta=10000.0):
+    return B.RopeSpec(d, (ctypes.c_int32 * 3)(*ax), theta)
+
+
+FAKE = 0x100000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("args,err", [
+    ((None, FAKE, 4, FAKE), "NULL"),
+    ((spec(96, (32, 32, 32)), FAKE, 4, FAKE), "UNSUPPORTED"),
+    ((spec(128, (32, 48, 46)), FAKE, 4, FAKE), "SHAPE"),
+    ((spec(128, (33, 47, 48)), FAKE, 4, FAKE), "SHAPE"),
+    ((spec(128, (32, 48, 48), -1.0), FAKE, 4, FAKE), "SHAPE"),
+    ((spec(), FAKE, -1, FAKE), "SHAPE"),
+    ((spec(), None, 4, FAKE), "NULL"),
+    ((spec(), FAKE, 4, FAKE + 8), "ALIGN"),
+])
+def test_rope_table_errors(L, args, err):
+    sp, pos, n, table = args
+    st = L.sa_make_rope_tables(None if sp is None else ctypes.byref(sp), pos, n, table, None)
+    assert st == ERR[err], L.sa_last_error()
+    assert L.sa_last_error() != b""
+
+
+def test_rope_table_empty_is_ok(L):
+    assert L.sa_make_rope_tables(ctypes.byref(spec()), None, 0, None, None) == 0
+    assert L.sa_last_error() == b""
+
+
+def test_packed_bytes(L):
+    n = ctypes.c_size_t()
+    assert L.sa_packed_bytes(40, 128, B.SA_BF16, 28480, ctypes.byref(n)) == 0
+    assert n.value == 40 * 28480 * 128 * 2
+    assert L.sa_packed_bytes(1, 64, B.SA_F32, 304, ctypes.byref(n)) == 0
+    assert n.value == 304 * 64 * 4
+    assert L.sa_packed_bytes(40, 128, B.SA_BF16, 28481, ctypes.byref(n)) == ERR["CAPACITY"]
+    assert L.sa_packed_bytes(40, 96, B.SA_BF16, 32, ctypes.byref(n)) == ERR["UNSUPPORTED"]
+    assert L.sa_packed_bytes(0, 128, B.SA_BF16, 32, ctypes.byref(n)) == ERR["SHAPE"]
+    assert L.sa_packed_bytes(4, 128, 7, 32, ctypes.byref(n)) == ERR["DTYPE"]
+    assert L.sa_packed_bytes(4, 128, B.SA_BF16, 32, None) == ERR["NULL"]
+
+
+def ctx(**kw):
+    c = dict(heads=2, head_dim=128, dtype=B.SA_BF16, capacity_rows=64, rows=48, k_packed=FAKE, v_packed=FAKE * 2)
+    c.update(kw)
+    return B.Context(c["heads"], c["head_dim"], c["dtype"], c["capacity_rows"], c["rows"], c["k_packed"],
+                     c["v_packed"])
+
+
+def seg(**kw):
+    s = dict(k=FAKE, v=FAKE, rows=16, k_row_stride=256, k_head_stride=128, v_row_stride=256, v_head_stride=128,
+             rope=None, dst_row=0)
+    s.update(kw)
+    return B.Segment(s["k"], s["v"], s["rows"], s["k_row_stride"], s["k_head_stride"], s["v_row_stride"],
+                     s["v_head_stride"], s["rope"], s["dst_row"])
+
+
+@pytest.mark.parametrize("c,segs,err", [
+    (None, [seg()], "NULL"),
+    (ctx(capacity_rows=60), [seg()], "CAPACITY"),
+    (ctx(rows=80), [seg()], "CAPACITY"),
+    (ctx(head_dim=96), [seg()], "UNSUPPORTED"),
+    (ctx(dtype=5), [seg()], "DTYPE"),
+    (ctx(heads=0), [seg()], "SHAPE"),
+    (ctx(k_packed=None), [seg()], "NULL"),
+    (ctx(k_packed=FAKE + 4), [seg()], "ALIGN"),
+    (ctx(), [seg(dst_row=40)], "SHAPE"),
+    (ctx(), [seg(dst_row=-1)], "SHAPE"),
+    (ctx(), [seg(rows=-2)], "SHAPE"),
+    (ctx(), [seg(), seg(dst_row=8)], "SHAPE"),
+    (ctx(), [seg(k=None)], "NULL"),
+    (ctx(), [seg(k=FAKE + 2)], "ALIGN"),
+    (ctx(), [seg(k_row_stride=260)], "ALIGN"),
+    (ctx(), [seg(k_head_stride=64)], "SHAPE"),
+    (ctx(), [seg(rope=FAKE + 4)], "ALIGN"),
+])
+def test_pack_errors(L, c, segs, err):
+    arr = (B.Segment * len(segs))(*segs)
+    st = L.sa_pack_context(None if c is None else ctypes.byref(c), arr, len(segs), None)
+    assert st == ERR[err], L.sa_last_error()
+
+
+def test_pack_segment_count_limits(L):
+    c = ctx()
+    arr = (B.Segment * 17)(*[seg(rows=0) for _ in range(17)])
+    assert L.sa_pack_context(ctypes.byref(c), arr, 17, None) == ERR["SHAPE"]
+    assert L.sa_pack_context(ctypes.byref(c), arr, -1, None) == ERR["SHAPE"]
+    assert L.sa_pack_context(ctypes.byref(c), None, 1, None) == ERR["NULL"]
+    # nothing to do: zero segments, or only empty ones, enqueue nothing
+    assert L.sa_pack_context(ctypes.byref(c), None, 0, None) == 0
+    assert L.sa_pack_context(ctypes.byref(c), arr, 16, None) == 0
+
+
+def fwd(L, c, q=FAKE, nq=8, qrs=256, qhs=128, rope=None, scale=0.1, out=FAKE * 3, odt=B.SA_BF16, ors=256,
+        ohs=128):
+    return L.sa_forward(None if c is None else ctypes.byref(c), q, nq, qrs, qhs, rope, scale, out, odt, ors, ohs,
+                        None)
+
+
+def test_forward_errors(L):
+    assert fwd(L, None) == ERR["NULL"]
+    assert fwd(L, ctx(rows=0)) == ERR["CAPACITY"]
+    assert fwd(L, ctx(), odt=9) == ERR["DTYPE"]
+    assert fwd(L, ctx(), nq=-1) == ERR["SHAPE"]
+    assert fwd(L, ctx(), scale=float("inf")) == ERR["SHAPE"]
+    assert fwd(L, ctx(), q=None) == ERR["NULL"]
+    assert fwd(L, ctx(), out=None) == ERR["NULL"]
+    assert fwd(L, ctx(), q=FAKE + 2) == ERR["ALIGN"]
+    assert fwd(L, ctx(), rope=FAKE + 4) == ERR["ALIGN"]
+    assert fwd(L, ctx(), qrs=250) == ERR["ALIGN"]
+    assert fwd(L, ctx(), odt=B.SA_F32, ors=258) == ERR["ALIGN"]
+    assert fwd(L, ctx(), qhs=64) == ERR["SHAPE"]
+    assert fwd(L, ctx(head_dim=64), ors=32) == ERR["SHAPE"]
+    # nq == 0 enqueues nothing and succeeds
+    assert fwd(L, ctx(), nq=0) == 0
+    assert L.sa_last_error() == b""

@@ -1,0 +1,140 @@
+"""Rotary tables and context packing against the oracle and the documented layout."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import note
+from oracle import rope64
+from streaming_video_diffusion_amd import binding as B
+from streaming_video_diffusion_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def perm16(j):
+    """Stored column j of a 16-row group holds row perm16(j) (layout of the packed V)."""
+    return [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15][j]
+
+
+def unpack_v_bf16(vt, heads, d, cap, rows):
+    """[H][d][C] with the 16-row column permutation -> [rows][H][d]."""
+    vt = vt.view(heads, d, cap)
+    cols = np.array([16 * (r // 16) + perm16(r % 16) for r in range(rows)])
+    return vt[:, :, torch.from_numpy(cols).cuda()].permute(2, 0, 1)
+
+
+@pytest.mark.parametrize("d,ax", [(128, (32, 48, 48)), (64, (16, 24, 24)), (128, (0, 64, 64))])
+def test_rope_tables_vs_oracle(d, ax):
+    note(f"[gpu] rope tables d={d} ax={ax}")
+    w = I.hier_1344x768()
+    pos = np.concatenate([w.q_pos, w.segments[2].pos, I.audio_positions(7, 40), w.segments[1].pos[:5]])
+    table = B.sa_make_rope_tables(torch.from_numpy(pos).cuda(), d, ax, 10000.0)
+    torch.cuda.synchronize()
+    got = table.cpu().numpy().astype(np.float64)
+    phi = rope64.angles(pos, ax, 10000.0)
+    assert np.max(np.abs(got[..., 0] - np.cos(phi))) <= 6e-8
+    assert np.max(np.abs(got[..., 1] - np.sin(phi))) <= 6e-8
+
+
+def _pack_case(dtype, d=128, heads=3):
+    w = I.custom("pack", 200, dtype, heads, d, [37, 64, 100], 10, prompt_rows=19)
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    ca = ChunkAttention(w)
+    ca.ctx.k_packed.fill_(float("nan"))
+    ca.ctx.v_packed.fill_(float("nan"))
+    ca.pack_static()
+    ca.step()
+    torch.cuda.synchronize()
+    return w, ca
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_pack_bf16_layout_and_rotation(d):
+    note(f"[gpu] pack bf16 d={d}")
+    w, ca = _pack_case("bf16", d=d)
+    cap, H = ca.ctx.capacity_rows, w.heads
+    kp = ca.ctx.k_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).float().cpu().numpy().astype(np.float64)
+    vp = unpack_v_bf16(ca.ctx.v_packed, H, d, cap, w.nk).float().cpu().numpy()
+    q, _, segs = ca.host_inputs()
+    row = 0
+    for (k, v, pos), s in zip(segs, w.segments):
+        ref = k.astype(np.float64) if pos is None else rope64.rotate(k, rope64.angles(pos, w.axis_dims, w.theta))
+        got = kp[row:row + s.rows]
+        # one rounding to bf16 of an fp32-computed rotation: <= 2^-8 relative (+ fp32 slack)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), s.name
+        if pos is None:
+            assert np.array_equal(got, ref), "prompt keys must be copied exactly"
+        assert np.array_equal(vp[row:row + s.rows], v), f"{s.name}: V must be copied bit-exactly"
+        row += s.rows
+    # rows past ctx.rows (up to capacity) are never written
+    tail = ca.ctx.k_packed.view(H, cap, d)[:, w.nk:]
+    assert torch.isnan(tail.float()).all()
+
+
+def test_pack_f32_layout_and_rotation():
+    note("[gpu] pack f32")
+    w, ca = _pack_case("f32")
+    cap, H, d = ca.ctx.capacity_rows, w.heads, w.head_dim
+    kp = ca.ctx.k_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy().astype(np.float64)
+    vp = ca.ctx.v_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy()
+    _, _, segs = ca.host_inputs()
+    row = 0
+    for (k, v, pos), s in zip(segs, w.segments):
+        ref = k.astype(np.float64) if pos is None else rope64.rotate(k, rope64.angles(pos, w.axis_dims, w.theta))
+        assert np.max(np.abs(kp[row:row + s.rows] - ref)) <= 2e-6, s.name
+        assert np.array_equal(vp[row:row + s.rows], v)
+        row += s.rows
+
+
+def test_dynamic_repack_leaves_static_rows_untouched():
+    note("[gpu] in-place dynamic repack")
+    w = I.lowres_bf16()
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    ca = ChunkAttention(w)
+    ca.pack_static()
+    ca.step()
+    torch.cuda.synchronize()
+    k0, v0 = ca.ctx.k_packed.clone(), ca.ctx.v_packed.clone()
+    n_static = sum(s.rows for s in w.segments if not s.dynamic)
+    for s in ca.segs:
+        if s["dynamic"]:
+            s["k"].mul_(-1.0)
+            s["v"].add_(1.0)
+    ca.step()
+    torch.cuda.synchronize()
+    H, d, cap = w.heads, w.head_dim, ca.ctx.capacity_rows
+    kv0, kv1 = k0.view(H, cap, d), ca.ctx.k_packed.view(H, cap, d)
+    assert torch.equal(kv0[:, :n_static], kv1[:, :n_static])
+    assert torch.equal(-kv0[:, n_static:w.nk], kv1[:, n_static:w.nk])
+    v0u = unpack_v_bf16(v0, H, d, cap, w.nk)
+    v1u = unpack_v_bf16(ca.ctx.v_packed, H, d, cap, w.nk)
+    assert torch.equal(v0u[:n_static], v1u[:n_static])
+    assert not torch.equal(v0u[n_static:], v1u[n_static:])
+
+
+def test_segment_split_gives_identical_packing():
+    note("[gpu] segment split")
+    w = I.lowres_bf16()
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    ca = ChunkAttention(w)
+    ca.pack_static()
+    ca.step()
+    torch.cuda.synchronize()
+    ref_k, ref_v, ref_o = ca.ctx.k_packed.clone(), ca.ctx.v_packed.clone(), ca.out.clone()
+    hist = next(s for s in ca.segs if s["name"] == "history")
+    ca.ctx.k_packed.zero_()
+    ca.ctx.v_packed.zero_()
+    segs = []
+    for s in ca.segs:
+        rope = ca.q_table if s["shares_q"] else s["table"]
+        if s is hist:
+            for a, b in ((0, 5), (5, 300), (300, s["k"].shape[0])):
+                segs.append((s["k"][a:b], s["v"][a:b], s["dst"] + a, None if rope is None else rope[a:b]))
+        else:
+            segs.append((s["k"], s["v"], s["dst"], rope))
+    B.sa_pack_context(ca.ctx, segs)
+    out = ca.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(ca.ctx.k_packed, ref_k) and torch.equal(ca.ctx.v_packed, ref_v)
+    assert torch.equal(out, ref_o)
