@@ -104,6 +104,8 @@ def _ptr(t):
 
 
 def _rows_heads(t, name):
+    if t.dim() == 3 and t.numel() == 0:
+        return t.shape[1] * t.shape[2], t.shape[2]   # nothing is read: nominal dense strides
     if t.dim() != 3 or t.stride(2) != 1:
         raise ValueError(f"{name} must be [rows][heads][head_dim] with a contiguous last dim")
     return t.stride(0), t.stride(1)

@@ -38,71 +38,71 @@ constexpr float kLazyRescale = 8.0f;  // log2 units
 
 __device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
-template <int D>
-struct Smem {
-    static constexpr int KP = D + 8;   // K tile row pitch (elements): rows land 4 banks apart
-    static constexpr int VP = BN + 8;  // V^T tile row pitch (elements)
-    static constexpr int KSZ = BN * KP;
-    static constexpr int VSZ = D * VP;
-    static constexpr int BUF = KSZ + VSZ;
-    static constexpr int BYTES = 2 * BUF * 2;
-};
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Physical 16-byte chunk of a tile row: XOR swizzles that keep the matrix-core
+// operand reads (32 rows, one logical chunk) free of LDS bank conflicts for
+// 32 or 64 banks. A 256-byte row swizzles by its low 4 row bits; a 128-byte
+// row (two rows per 64 banks) by ((r >> 1) & 7) ^ ((r & 1) << 2).
+__device__ __forceinline__ int swz256(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz128(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
 
 template <int D>
-struct TileLoader {
-    // K tile: BN rows x D, 16-byte chunks; V^T tile: D rows x BN keys.
-    static constexpr int KCH = D / 8;
-    static constexpr int KLOADS = BN * KCH / kThreads;
-    static constexpr int VCH = BN / 8;
-    static constexpr int VLOADS = D * VCH / kThreads;
-    bf16x8 kr[KLOADS];
-    bf16x8 vr[VLOADS];
+struct Tile {
+    static constexpr int KROW = D * 2;          // bytes per K row
+    static constexpr int VROW = BN * 2;         // bytes per V^T row (128)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int VBYTES = D * VROW;
+    static constexpr int BUF = KBYTES + VBYTES;  // bytes per buffer
+    static constexpr int BYTES = 2 * BUF;
+    static constexpr int KINSTR = KBYTES / 1024;  // 1 KiB per wave-wide direct load
+    static constexpr int VINSTR = VBYTES / 1024;
+    static constexpr int KROWS_PER_INSTR = 1024 / KROW;
+    static constexpr int VROWS_PER_INSTR = 1024 / VROW;
 
-    __device__ __forceinline__ void load(const bf16 *__restrict__ kb, const bf16 *__restrict__ vb, int64_t cap,
-                                         int64_t k0, int64_t nk, bool last, int t) {
+    __device__ static __forceinline__ int kswz(int r, int c) { return D == 128 ? swz256(r, c) : swz128(r, c); }
+    // byte offset of logical chunk c of K row r / V^T row r inside a buffer
+    __device__ static __forceinline__ int koff(int r, int c) { return r * KROW + kswz(r, c) * 16; }
+    __device__ static __forceinline__ int voff(int r, int c) { return KBYTES + r * VROW + swz128(r, c) * 16; }
+
+    // Issue this wave's share of the direct global->LDS loads of one K/V^T tile.
+    // In the last (ragged) tile, rows / column groups past nk are clamped to
+    // in-bounds addresses; their contents are masked or zeroed afterwards.
+    __device__ static __forceinline__ void issue(unsigned char *buf, const bf16 *__restrict__ kb,
+                                                 const bf16 *__restrict__ vb, int64_t cap, int64_t k0, int64_t nk,
+                                                 bool last, int w, int lane) {
 #pragma unroll
-        for (int i = 0; i < KLOADS; ++i) {
-            const int id = t + i * kThreads;
-            const int row = id / KCH, ch = id % KCH;
-            const int64_t key = k0 + row;
-            if (!last || key < nk)
-                kr[i] = *reinterpret_cast<const bf16x8 *>(kb + key * D + ch * 8);
-            else
-                kr[i] = bf16x8{};
+        for (int ii = 0; ii < KINSTR / kWaves; ++ii) {
+            const int i = w * (KINSTR / kWaves) + ii;
+            const int r = i * KROWS_PER_INSTR + lane / (KROW / 16);
+            const int p = lane % (KROW / 16);
+            int64_t key = k0 + r;
+            if (last && key >= nk) key = nk - 1;
+            const bf16 *src = kb + key * D + kswz(r, p) * 8;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int id = t + i * kThreads;
-            const int dr = id / VCH, ch = id % VCH;
-            const int64_t col0 = k0 + ch * 8;
-            if (!last) {
-                vr[i] = *reinterpret_cast<const bf16x8 *>(vb + (int64_t)dr * cap + col0);
-            } else if ((col0 & ~int64_t(15)) < nk) {
-                bf16x8 x = *reinterpret_cast<const bf16x8 *>(vb + (int64_t)dr * cap + col0);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int64_t key = (col0 & ~int64_t(15)) + group_perm((int)(col0 & 15) + jj);
-                    if (key >= nk) x[jj] = (bf16)0.0f;
-                }
-                vr[i] = x;
-            } else {
-                vr[i] = bf16x8{};
-            }
+        for (int ii = 0; ii < VINSTR / kWaves; ++ii) {
+            const int i = w * (VINSTR / kWaves) + ii;
+            const int r = i * VROWS_PER_INSTR + lane / 8;
+            const int p = lane % 8;
+            int64_t col = k0 + swz128(r, p) * 8;
+            if (last && (col & ~int64_t(15)) >= nk) col = k0;
+            const bf16 *src = vb + (int64_t)r * cap + col;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + KBYTES + i * 1024), 16, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void store(bf16 *sk, bf16 *sv, int t) const {
-#pragma unroll
-        for (int i = 0; i < KLOADS; ++i) {
-            const int id = t + i * kThreads;
-            const int row = id / KCH, ch = id % KCH;
-            *reinterpret_cast<bf16x8 *>(sk + row * Smem<D>::KP + ch * 8) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int id = t + i * kThreads;
-            const int dr = id / VCH, ch = id % VCH;
-            *reinterpret_cast<bf16x8 *>(sv + dr * Smem<D>::VP + ch * 8) = vr[i];
+    // Zero the V^T entries of keys >= nk in the last tile (P is 0 there, but the
+    // packed buffer past nk is never written and may hold non-finite bits).
+    __device__ static __forceinline__ void zero_tail(unsigned char *buf, int64_t k0, int64_t nk, int t) {
+        for (int e = t; e < D * BN; e += kThreads) {
+            const int r = e / BN, sc = e % BN;  // d-row, stored column
+            const int64_t key = k0 + (sc & ~15) + group_perm(sc & 15);
+            if (key >= nk) {
+                bf16 *q = reinterpret_cast<bf16 *>(buf + voff(r, sc >> 3)) + (sc & 7);
+                *q = (bf16)0.0f;
+            }
         }
     }
 };
@@ -111,8 +111,7 @@ template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
     constexpr int DC = D / 16;  // k-steps of Q.K^T
     constexpr int DT = D / 32;  // 32-row d tiles of O^T
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+    extern __shared__ __align__(1024) unsigned char smem[];
 
     // XCD-aware workgroup -> (head, query tile) map: consecutive dispatch ids
     // go round-robin over the 8 XCDs; give each XCD a contiguous logical range.
@@ -178,16 +177,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int ntiles = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
 
-    TileLoader<D> ld;
-    ld.load(kb, vb, a.cap, 0, a.nk, ntiles == 1, t);
-    ld.store(smem, smem + Smem<D>::KSZ, t);
+    // wave-uniform wave index (selects this wave's share of the tile loads)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    Tile<D>::issue(smem, kb, vb, a.cap, 0, a.nk, ntiles == 1, wu, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads landed
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
-        bf16 *sk = smem + (kt & 1) * Smem<D>::BUF;
-        bf16 *sv = sk + Smem<D>::KSZ;
-        const bool has_next = kt + 1 < ntiles;
-        if (has_next) ld.load(kb, vb, a.cap, (int64_t)(kt + 1) * BN, a.nk, kt + 2 == ntiles, t);
+        unsigned char *buf = smem + (kt & 1) * Tile<D>::BUF;
+        if (ragged && kt + 1 == ntiles) {
+            Tile<D>::zero_tail(buf, (int64_t)kt * BN, a.nk, t);
+            __syncthreads();
+        }
+        if (kt + 1 < ntiles)
+            Tile<D>::issue(smem + ((kt + 1) & 1) * Tile<D>::BUF, kb, vb, a.cap, (int64_t)(kt + 1) * BN, a.nk,
+                           kt + 2 == ntiles, wu, lane);
 
         // ---- S^T = K Q^T ---------------------------------------------------
         f32x16 s[2][2];
@@ -197,8 +201,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int u = 0; u < 2; ++u) s[tt][u] = f32x16{};
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(sk + l32 * Smem<D>::KP + 16 * j + 8 * hf);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(sk + (32 + l32) * Smem<D>::KP + 16 * j + 8 * hf);
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(buf + Tile<D>::koff(l32, 2 * j + hf));
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(buf + Tile<D>::koff(32 + l32, 2 * j + hf));
             s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0][j], s[0][0], 0, 0, 0);
             s[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[1][j], s[0][1], 0, 0, 0);
             s[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0][j], s[1][0], 0, 0, 0);
@@ -267,15 +271,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
                     const bf16x8 va =
-                        *reinterpret_cast<const bf16x8 *>(sv + (32 * c + l32) * Smem<D>::VP + 32 * tt + 16 * g + 8 * hf);
+                        *reinterpret_cast<const bf16x8 *>(buf + Tile<D>::voff(32 * c + l32, 4 * tt + 2 * g + hf));
                     o[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tt][g][0], o[c][0], 0, 0, 0);
                     o[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tt][g][1], o[c][1], 0, 0, 0);
                 }
 
-        if (has_next) {
-            bf16 *nk_s = smem + ((kt + 1) & 1) * Smem<D>::BUF;
-            ld.store(nk_s, nk_s + Smem<D>::KSZ, t);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's direct loads landed
         __syncthreads();
     }
 
@@ -319,9 +320,9 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,
     // idempotent, no stream work).
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Smem<D>::BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Tile<D>::BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kThreads), Smem<D>::BYTES, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kThreads), Tile<D>::BYTES, stream, a);
     return hipGetLastError();
 }
 
