@@ -53,8 +53,8 @@ extern "C" {
 
 #define SA_ABI_VERSION 1
 
-/* Packed context capacity (rows) must be a multiple of this. */
-#define SA_ROW_ALIGN 16
+/* Packed context capacity (rows) must be a multiple of this (one key tile). */
+#define SA_ROW_ALIGN 64
 /* Most segments one sa_pack_context call accepts. */
 #define SA_MAX_SEGMENTS 16
 
@@ -135,13 +135,16 @@ typedef struct {
  *               matrix-core lane reads its 8 keys as one 16-byte vector.
  *   SA_F32:  K  float32 [H][C][d] rotated; V float32 [H][C][d].
  * rows (Nk) is the number of valid packed rows; the forward pass attends to
- * rows [0, rows) and never reads past them (up to the next multiple of 16).
+ * rows [0, rows). It reads whole 64-row tiles, so it also loads (and then
+ * ignores) the rows up to the next multiple of SA_ROW_ALIGN; their contents
+ * never reach the result.
  */
 typedef struct {
     int32_t heads;         /* >= 1 */
     int32_t head_dim;      /* 64 or 128 */
     sa_dtype dtype;        /* element type of K, V (and of Q in sa_forward) */
-    int64_t capacity_rows; /* allocated rows, a multiple of SA_ROW_ALIGN */
+    int64_t capacity_rows; /* allocated rows, a multiple of SA_ROW_ALIGN; one head's packed
+                              K (or V), capacity_rows * head_dim * element size, at most 2^31 bytes */
     int64_t rows;          /* valid rows Nk, 1 <= rows <= capacity_rows for sa_forward */
     void *k_packed;        /* device, sa_packed_bytes() bytes */
     void *v_packed;        /* device, sa_packed_bytes() bytes */
@@ -150,7 +153,8 @@ typedef struct {
 /*
  * sa_packed_bytes -- size in bytes of each of k_packed and v_packed.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
- * SA_ERR_CAPACITY (capacity_rows not a multiple of SA_ROW_ALIGN).
+ * SA_ERR_CAPACITY (capacity_rows not a multiple of SA_ROW_ALIGN, or one head's
+ * packed K/V above 2^31 bytes).
  */
 sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64_t capacity_rows,
                           size_t *bytes_each);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamat
 SA_OK = 0
 SA_F32 = 0
 SA_BF16 = 1
-SA_ROW_ALIGN = 16
+SA_ROW_ALIGN = 64
 SA_MAX_SEGMENTS = 16
 
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}

@@ -38,6 +38,20 @@ namespace sa {
 namespace {
 
 constexpr int BN = 64;                // keys per tile
+#ifndef SA_FWD_STAGES
+#define SA_FWD_STAGES 2
+#endif
+constexpr int NS = SA_FWD_STAGES;     // K/V pipeline stages in LDS
+static_assert(NS >= 2 && NS <= 4, "2..4 pipeline stages");
+#ifndef SA_FWD_UNROLL_STAGES
+#define SA_FWD_UNROLL_STAGES 0
+#endif
+#ifndef SA_FWD_EARLY_V
+#define SA_FWD_EARLY_V 0
+#endif
+#ifndef SA_FWD_PREFETCH
+#define SA_FWD_PREFETCH 1
+#endif
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 __device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
@@ -58,48 +72,75 @@ struct Tile {
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = D * VROW;
     static constexpr int BUF = KBYTES + VBYTES;  // bytes per buffer
-    static constexpr int BYTES = 2 * BUF;
+    static constexpr int BYTES = NS * BUF;
     static constexpr int KINSTR = KBYTES / 1024;  // 1 KiB per wave-wide direct load
     static constexpr int VINSTR = VBYTES / 1024;
     static constexpr int KROWS_PER_INSTR = 1024 / KROW;
     static constexpr int VROWS_PER_INSTR = 1024 / VROW;
     static_assert(KINSTR % NW == 0 && VINSTR % NW == 0, "tile loads must split evenly over the waves");
+    static constexpr int LOADS_PER_WAVE = KINSTR / NW + VINSTR / NW;
+    static_assert(LOADS_PER_WAVE < 16, "vmcnt immediate");
+    // wait until at most n tiles' loads (the newest) are still in flight
+    __device__ static __forceinline__ void wait_tiles_in_flight(int n) {
+        if (n <= 0)
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        else if (n == 1)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_WAVE);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS_PER_WAVE));
+    }
 
     __device__ static __forceinline__ int kswz(int r, int c) { return D == 128 ? swz256(r, c) : swz128(r, c); }
     // byte offset of logical chunk c of K row r / V^T row r inside a buffer
     __device__ static __forceinline__ int koff(int r, int c) { return r * KROW + kswz(r, c) * 16; }
     __device__ static __forceinline__ int voff(int r, int c) { return KBYTES + r * VROW + swz128(r, c) * 16; }
 
-    // Issue this wave's share of the direct global->LDS loads of one K/V^T tile.
-    // In the last (ragged) tile, rows / column groups past nk are clamped to
-    // in-bounds addresses; their contents are masked or zeroed afterwards.
-    __device__ static __forceinline__ void issue(unsigned char *buf, const bf16 *__restrict__ kb,
-                                                 const bf16 *__restrict__ vb, int64_t cap, int64_t k0, int64_t nk,
-                                                 bool last, int w, int lane) {
+    // Loop-invariant per-lane byte offsets of this wave's share of one tile's
+    // direct global->LDS loads (K relative to the tile's first K row, V^T
+    // relative to the tile's first V^T column), so each tile only moves a
+    // wave-uniform base pointer.
+    struct Plan {
+        uint32_t k[KINSTR / NW];
+        uint32_t v[VINSTR / NW];
+    };
+    __device__ static __forceinline__ Plan plan(int64_t cap, int w, int lane) {
+        Plan pl;
 #pragma unroll
         for (int ii = 0; ii < KINSTR / NW; ++ii) {
             const int i = w * (KINSTR / NW) + ii;
             const int r = i * KROWS_PER_INSTR + lane / (KROW / 16);
-            const int p = lane % (KROW / 16);
-            int64_t key = k0 + r;
-            if (last && key >= nk) key = nk - 1;
-            const bf16 *src = kb + key * D + kswz(r, p) * 8;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, 0);
+            pl.k[ii] = (uint32_t)(r * KROW + kswz(r, lane % (KROW / 16)) * 16);
         }
 #pragma unroll
         for (int ii = 0; ii < VINSTR / NW; ++ii) {
             const int i = w * (VINSTR / NW) + ii;
             const int r = i * VROWS_PER_INSTR + lane / 8;
-            const int p = lane % 8;
-            int64_t col = k0 + swz128(r, p) * 8;
-            if (last && (col & ~int64_t(15)) >= nk) col = k0;
-            const bf16 *src = vb + (int64_t)r * cap + col;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + KBYTES + i * 1024), 16, 0, 0);
+            pl.v[ii] = (uint32_t)(r * cap * 2 + swz128(r, lane % 8) * 16);
         }
+        return pl;
+    }
+
+    // Issue this wave's share of the direct global->LDS loads of one K/V^T
+    // tile: a wave-uniform tile base plus the loop-invariant lane offsets. The
+    // packed capacity is a multiple of the tile, so the last tile never leaves
+    // the allocation; its rows past nk are masked (K) or zeroed (V^T) after.
+    __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, const unsigned char *kb,
+                                                 const unsigned char *vb, int64_t k0, int w) {
+        const unsigned char *kt = kb + k0 * KROW;
+        const unsigned char *vt = vb + k0 * 2;
+#pragma unroll
+        for (int ii = 0; ii < KINSTR / NW; ++ii)
+            __builtin_amdgcn_global_load_lds(kt + pl.k[ii], (lds_void *)(buf + (w * (KINSTR / NW) + ii) * 1024), 16,
+                                             0, 0);
+#pragma unroll
+        for (int ii = 0; ii < VINSTR / NW; ++ii)
+            __builtin_amdgcn_global_load_lds(vt + pl.v[ii],
+                                             (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024), 16, 0, 0);
     }
 
     // Zero the V^T entries of keys >= nk in the last tile (P is 0 there, but the
-    // packed buffer past nk is never written and may hold non-finite bits).
+    // packed rows past nk are not written by the pack and may hold non-finite
+    // bits).
     __device__ static __forceinline__ void zero_tail(unsigned char *buf, int64_t k0, int64_t nk, int t) {
         for (int e = t; e < D * BN; e += NW * 64) {
             const int r = e / BN, sc = e % BN;  // d-row, stored column
@@ -113,6 +154,14 @@ struct Tile {
 };
 
 __device__ __forceinline__ void vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Value of lane l ^ 32 (the other half-wave holds the same query column).
+__device__ __forceinline__ float half_swap_partner(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // r[0]: lanes 32..63 took lanes 0..31; r[1]: lanes 0..31 took lanes 32..63
+    return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
+}
 
 template <int D, int NW, int U, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -183,51 +232,78 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int c = 0; c < DT; ++c)
 #pragma unroll
         for (int u = 0; u < U; ++u) o[c][u] = f32x16{};
-    float m[U], l[U];
-    f32x16 negm[U];
+    float l[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        m[u] = 0.f;
-        l[u] = 0.f;
-        negm[u] = f32x16{};
-    }
+    for (int u = 0; u < U; ++u) l[u] = 0.f;
 
-    const bf16 *kb = reinterpret_cast<const bf16 *>(a.k) + (int64_t)head * a.cap * D;
-    const bf16 *vb = reinterpret_cast<const bf16 *>(a.v) + (int64_t)head * D * a.cap;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)head * a.cap * D * 2;
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(a.v) + (int64_t)head * D * a.cap * 2;
     const int ntiles = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    T::issue(smem, kb, vb, a.cap, 0, a.nk, ntiles == 1, wu, lane);
-    vmcnt0();
+    // NS-stage K/V pipeline: tiles kt+1 .. kt+NS-1 are in flight while tile kt
+    // is used.
+    for (int p = 0; p < NS - 1 && p < ntiles; ++p)
+        T::issue(smem + p * T::BUF, T::plan(a.cap, wu, lane), kb, vb, (int64_t)p * BN, wu);
+    T::wait_tiles_in_flight(min(NS - 2, ntiles - 1));
     __syncthreads();
 
-    // One K/V tile. The hot variant has no O rescale (which would keep two
-    // copies of the O accumulators live); a wave whose running max would have
-    // to rise returns false before touching P, and redoes the tile, and the
-    // rest, in the cold variant. Both variants meet exactly one end-of-tile
-    // barrier per tile; `redo` skips the last tile's zeroing barrier that the
-    // hot variant already passed.
-    auto body = [&](auto hot_tag, const int kt, unsigned char *buf, unsigned char *nbuf,
-                    const bool redo) __attribute__((always_inline)) -> bool {
+    // Running max m (log2 units, per query). The hot variant keeps m = 0 and
+    // seeds the score accumulator with the constant 0: it is exact as long as
+    // every tile max stays below 2^8 (and the first tile's above 2^-8), which
+    // bounds P by 256 and keeps the sum far from under/overflow. A wave that
+    // sees a tile outside that band returns false before touching P and
+    // redoes that tile, and the rest, in the cold variant, which carries m
+    // explicitly and rescales O and l when it must rise. Keeping the O
+    // rescale out of the hot variant keeps a second copy of the O
+    // accumulators out of its live set. Both variants meet exactly one
+    // end-of-tile barrier per tile; `redo` skips the tile's load issue and
+    // the last tile's zeroing barrier that the hot variant already passed.
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    // m / negm: running max and its negation broadcast over an accumulator
+    // (cold variant only; the hot variant never touches them, so they are not
+    // live across the hot loop).
+    auto body = [&](auto hot_tag, const int kt, unsigned char *buf, unsigned char *nbuf, const bool redo,
+                    float *m, f32x16 *negm) __attribute__((always_inline)) -> bool {
         constexpr bool HOT = decltype(hot_tag)::value;
+        // Per-lane LDS and global offsets are recomputed from an opaque copy of
+        // the lane id every tile (a dozen VALU ops) instead of being hoisted
+        // out of the loop, where they would crowd the register file.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l32 = ln & 31, hf = ln >> 5;
         if (ragged && kt + 1 == ntiles && !redo) {
             T::zero_tail(buf, (int64_t)kt * BN, a.nk, t);
             __syncthreads();
         }
-        if (kt + 1 < ntiles)
-            T::issue(nbuf, kb, vb, a.cap, (int64_t)(kt + 1) * BN, a.nk, kt + 2 == ntiles, wu, lane);
+        if (kt + NS - 1 < ntiles && !redo)
+            T::issue(nbuf, T::plan(a.cap, wu, ln), kb, vb, (int64_t)(kt + NS - 1) * BN, wu);
 
-        // ---- S^T - m = K Q^T + (-m) ------------------------------------------
+        // ---- S^T (log2 units, minus m) = K Q^T + (-m) ----------------------
         f32x16 s[2][U];
+        bf16x8 ka0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, hf));
+        bf16x8 ka1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, hf));
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, 2 * j + hf));
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, 2 * j + hf));
+            bf16x8 kn0, kn1;
+            if (SA_FWD_PREFETCH && j + 1 < DC) {
+                kn0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, 2 * (j + 1) + hf));
+                kn1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, 2 * (j + 1) + hf));
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                s[0][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[u][j], j == 0 ? negm[u] : s[0][u], 0, 0, 0);
-                s[1][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[u][j], j == 0 ? negm[u] : s[1][u], 0, 0, 0);
+                const f32x16 c0 = j ? s[0][u] : (HOT ? f32x16{} : negm[u]);
+                const f32x16 c1 = j ? s[1][u] : (HOT ? f32x16{} : negm[u]);
+                s[0][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[u][j], c0, 0, 0, 0);
+                s[1][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[u][j], c1, 0, 0, 0);
+            }
+            if (SA_FWD_PREFETCH && j + 1 < DC) {
+                ka0 = kn0;
+                ka1 = kn1;
+            } else if (j + 1 < DC) {
+                ka0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, 2 * (j + 1) + hf));
+                ka1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, 2 * (j + 1) + hf));
             }
         }
 
@@ -246,7 +322,12 @@ void fwd_bf16_kernel(FwdArgs a) {
                 }
         }
 
-        // ---- online softmax (log2 domain, lazily raised running max) ---------
+#if SA_FWD_EARLY_V
+        // first V^T operand, read while the softmax runs
+        bf16x8 va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(l32, hf));
+#endif
+
+        // ---- online softmax ---------------------------------------------------
         bf16x8 pb[2][2][U];  // [key subtile][16-key group][query subtile]
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -255,15 +336,19 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][u][i]);
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][u][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));  // tile max of s - m for this query
-            if (kt == 0) {
-                // first tile: adopt its max (O and l are still zero)
-                m[u] = mx;
+            mx = fmaxf(mx, half_swap_partner(mx));  // tile max of s - m for this query
+            if (HOT) {
+                if (__any(mx > kLazyRescale || (kt == 0 && mx < -kLazyRescale))) return false;
+            } else if (kt == 0) {
+                // no accumulation yet: a lane outside the band adopts its first
+                // tile's max; the others keep m = 0 and match the hot variant
+                // bit for bit
+                const float delta = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
+                m[u] = delta;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) s[tt][u] -= mx;
-                negm[u] = -mx;
+                for (int tt = 0; tt < 2; ++tt) s[tt][u] -= delta;
+                negm[u] = -delta;
             } else if (__any(mx > kLazyRescale)) {
-                if (HOT) return false;
                 const float delta = mx > kLazyRescale ? mx : 0.0f;
                 const float alpha = __builtin_amdgcn_exp2f(-delta);
                 l[u] *= alpha;
@@ -274,7 +359,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) s[tt][u] -= delta;
             }
-            float ls = 0.f;
+            float ls[2] = {0.f, 0.f};
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -285,52 +370,86 @@ void fwd_bf16_kernel(FwdArgs a) {
                         bf16x2 pp;
                         pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][u][8 * g + e]);
                         pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][u][8 * g + e + 1]);
-                        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+                        ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
                         pv[e] = pp.x;
                         pv[e + 1] = pp.y;
                     }
                     pb[tt][g][u] = pv;
                 }
-            l[u] += ls;
+            l[u] += ls[0] + ls[1];
         }
 
         // ---- O^T += V^T P^T ---------------------------------------------------
+#if !SA_FWD_EARLY_V
+        bf16x8 va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(l32, hf));
+#endif
 #pragma unroll
-        for (int c = 0; c < DT; ++c)
+        for (int idx = 0; idx < DT * 4; ++idx) {
+            const int c = idx >> 2, tt = (idx >> 1) & 1, g = idx & 1;
+            bf16x8 vn;
+            if (SA_FWD_PREFETCH && idx + 1 < DT * 4) {
+                const int c2 = (idx + 1) >> 2, tt2 = ((idx + 1) >> 1) & 1, g2 = (idx + 1) & 1;
+                vn = *reinterpret_cast<const bf16x8 *>(buf + T::voff(32 * c2 + l32, 4 * tt2 + 2 * g2 + hf));
+            }
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const bf16x8 va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(32 * c + l32, 4 * tt + 2 * g + hf));
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        o[c][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tt][g][u], o[c][u], 0, 0, 0);
-                }
+            for (int u = 0; u < U; ++u)
+                o[c][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tt][g][u], o[c][u], 0, 0, 0);
+            if (SA_FWD_PREFETCH && idx + 1 < DT * 4) {
+                va = vn;
+            } else if (idx + 1 < DT * 4) {
+                const int c2 = (idx + 1) >> 2, tt2 = ((idx + 1) >> 1) & 1, g2 = (idx + 1) & 1;
+                va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(32 * c2 + l32, 4 * tt2 + 2 * g2 + hf));
+            }
+        }
 
-        vmcnt0();  // this wave's share of the next tile has landed
+        // the next tile's loads have landed (later tiles may still be in flight)
+        T::wait_tiles_in_flight(min(NS - 2, ntiles - 2 - kt));
         __syncthreads();
         return true;
     };
 
     typedef std::integral_constant<bool, true> Hot;
     typedef std::integral_constant<bool, false> Cold;
+    constexpr int SB = T::BUF;
     int kt = 0;
-    for (; kt < ntiles; kt += 2) {
-        if (!body(Hot(), kt, smem, smem + T::BUF, false)) break;
-        if (kt + 1 < ntiles && !body(Hot(), kt + 1, smem + T::BUF, smem, false)) {
-            ++kt;
-            break;
+#if SA_FWD_UNROLL_STAGES
+    bool left_hot = false;
+    for (; kt < ntiles && !left_hot; kt += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (kt + i < ntiles &&
+                !body(Hot(), kt + i, smem + i * SB, smem + ((i + NS - 1) % NS) * SB, false, nullptr, nullptr)) {
+                kt += i;
+                left_hot = true;
+                break;
+            }
         }
     }
-    // Cold path (rare): a tile raised this wave's running max by more than
-    // 2^8; redo it with rescaling, then finish the remaining tiles.
-    for (bool redo = true; kt < ntiles; ++kt, redo = false)
-        body(Cold(), kt, smem + (kt & 1) * T::BUF, smem + ((kt + 1) & 1) * T::BUF, redo);
+    if (left_hot) kt -= NS;  // undo the loop increment taken on exit
+#else
+    for (int st = 0; kt < ntiles; ++kt, st = (st + 1 == NS ? 0 : st + 1)) {
+        const int nst = st == 0 ? NS - 1 : st - 1;  // stage of tile kt + NS - 1
+        if (!body(Hot(), kt, smem + st * SB, smem + nst * SB, false, nullptr, nullptr)) break;
+    }
+#endif
+    // Cold path (rare): redo the tile that left the hot band, then finish. The
+    // hot variant kept m = 0, so the cold variant starts from there.
+    if (kt < ntiles) {
+        float m[U];
+        f32x16 negm[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            m[u] = 0.f;
+            negm[u] = f32x16{};
+        }
+        for (bool redo = true; kt < ntiles; ++kt, redo = false)
+            body(Cold(), kt, smem + (kt % NS) * SB, smem + ((kt + NS - 1) % NS) * SB, redo, m, negm);
+    }
 
     // ---- epilogue: O / l, store ----------------------------------------------
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const float lt = l[u] + __shfl_xor(l[u], 32);
+        const float lt = l[u] + half_swap_partner(l[u]);
         const float inv = 1.0f / lt;
         const int64_t row = q_base + 32 * u + l32;
         if (row >= a.nq) continue;

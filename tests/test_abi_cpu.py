@@ -92,8 +92,9 @@ def test_packed_bytes(L):
     n = ctypes.c_size_t()
     assert L.sa_packed_bytes(40, 128, B.SA_BF16, 28480, ctypes.byref(n)) == 0
     assert n.value == 40 * 28480 * 128 * 2
-    assert L.sa_packed_bytes(1, 64, B.SA_F32, 304, ctypes.byref(n)) == 0
-    assert n.value == 304 * 64 * 4
+    assert L.sa_packed_bytes(1, 64, B.SA_F32, 320, ctypes.byref(n)) == 0
+    assert n.value == 320 * 64 * 4
+    assert L.sa_packed_bytes(1, 64, B.SA_F32, 304, ctypes.byref(n)) == ERR["CAPACITY"]
     assert L.sa_packed_bytes(40, 128, B.SA_BF16, 28481, ctypes.byref(n)) == ERR["CAPACITY"]
     assert L.sa_packed_bytes(40, 96, B.SA_BF16, 32, ctypes.byref(n)) == ERR["UNSUPPORTED"]
     assert L.sa_packed_bytes(0, 128, B.SA_BF16, 32, ctypes.byref(n)) == ERR["SHAPE"]
@@ -120,6 +121,7 @@ def seg(**kw):
     (None, [seg()], "NULL"),
     (ctx(capacity_rows=60), [seg()], "CAPACITY"),
     (ctx(rows=80), [seg()], "CAPACITY"),
+    (ctx(capacity_rows=48, rows=40), [seg()], "CAPACITY"),
     (ctx(head_dim=96), [seg()], "UNSUPPORTED"),
     (ctx(dtype=5), [seg()], "DTYPE"),
     (ctx(heads=0), [seg()], "SHAPE"),
