@@ -34,7 +34,23 @@ def parse():
     p.add_argument("--workload", default="full_1344x768")
     p.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (3 times) and exit; "
+                        "its FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size (read mib MiB, write mib MiB), for
+    scaling the profiler's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 3}), flush=True)
 
 
 def cpu_baseline(w, rows_n):
@@ -77,6 +93,9 @@ def cpu_baseline(w, rows_n):
 
 def main():
     args = parse()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the attention shards by head; see the design notes). Run with --gpus 1.", file=sys.stderr)

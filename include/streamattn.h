@@ -135,9 +135,10 @@ typedef struct {
  *               matrix-core lane reads its 8 keys as one 16-byte vector.
  *   SA_F32:  K  float32 [H][C][d] rotated; V float32 [H][C][d].
  * rows (Nk) is the number of valid packed rows; the forward pass attends to
- * rows [0, rows). It reads whole 64-row tiles, so it also loads (and then
- * ignores) the rows up to the next multiple of SA_ROW_ALIGN; their contents
- * never reach the result.
+ * rows [0, rows). It reads whole 64-row tiles, so it also loads the padding
+ * rows up to the next multiple of SA_ROW_ALIGN: their keys are masked and
+ * their values are multiplied by zero weights, so they must hold finite
+ * numbers; sa_pack_context writes zeros there.
  */
 typedef struct {
     int32_t heads;         /* >= 1 */
@@ -164,10 +165,12 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
  *
  * Each segment's rows are written to packed rows [dst_row, dst_row + rows),
  * keys rotated by the segment's table (fused into the load: no separate RoPE
- * pass), values copied (bf16: transposed as documented above). Packed rows
- * not covered by a segment of this call are left untouched, so the static
- * prefix (prompt, reference) can be packed once per bank and the dynamic
- * region (history, current chunk) rewritten in place every chunk.
+ * pass), values copied (bf16: transposed as documented above). A call that
+ * packs at least one row also writes zeros to the padding rows [ctx->rows,
+ * next multiple of SA_ROW_ALIGN) of every head. Other packed rows not covered
+ * by a segment of this call are left untouched, so the static prefix (prompt,
+ * reference) can be packed once per bank and the dynamic region (history,
+ * current chunk) rewritten in place every chunk.
  * Segment row ranges must lie inside [0, ctx->rows) and must not overlap.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE (n_segs outside [0, SA_MAX_SEGMENTS],
  * ranges, strides), SA_ERR_CAPACITY, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,

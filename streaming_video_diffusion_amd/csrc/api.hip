@@ -192,8 +192,12 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
         if (tiles > max_tiles) max_tiles = tiles;
     }
     a.n_segs = used;
+    if (used == 0) return SA_OK;
     hipError_t e = sa::launch_pack(a, ctx->head_dim, ctx->dtype, max_tiles, stream);
     if (e != hipSuccess) return hip_fail(e, "pack launch");
+    const int64_t pad_end = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN * SA_ROW_ALIGN;
+    e = sa::launch_zero_pad(a, ctx->head_dim, ctx->dtype, ctx->rows, pad_end, stream);
+    if (e != hipSuccess) return hip_fail(e, "pad launch");
     return SA_OK;
 }
 
@@ -237,7 +241,7 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
     a.out_f32 = out_dtype == SA_F32;
     a.scale = softmax_scale;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-    const int64_t rows_per_wg = ctx->dtype == SA_BF16 ? 256 : 64;
+    const int64_t rows_per_wg = ctx->dtype == SA_BF16 ? sa::fwd_bf16_rows_per_workgroup() : sa::kFwdF32RowsPerWorkgroup;
     const int64_t blocks = ((nq + rows_per_wg - 1) / rows_per_wg) * ctx->heads;
     if (blocks > 0x7fffffff) return fail(SA_ERR_SHAPE, "nq x heads too large for one grid");
     hipError_t e = ctx->dtype == SA_BF16 ? sa::launch_fwd_bf16(a, ctx->head_dim, stream)

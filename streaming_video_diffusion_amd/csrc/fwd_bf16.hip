@@ -37,24 +37,15 @@ namespace sa {
 
 namespace {
 
-constexpr int BN = 64;                // keys per tile
-#ifndef SA_FWD_STAGES
-#define SA_FWD_STAGES 2
+#ifndef SA_FWD_HAND
+#define SA_FWD_HAND 1
 #endif
-constexpr int NS = SA_FWD_STAGES;     // K/V pipeline stages in LDS
-static_assert(NS >= 2 && NS <= 4, "2..4 pipeline stages");
-#ifndef SA_FWD_UNROLL_STAGES
-#define SA_FWD_UNROLL_STAGES 0
+#ifndef SA_FWD_SGB
+#define SA_FWD_SGB 0
 #endif
-#ifndef SA_FWD_EARLY_V
-#define SA_FWD_EARLY_V 0
-#endif
-#ifndef SA_FWD_PREFETCH
-#define SA_FWD_PREFETCH 1
-#endif
-constexpr float kLazyRescale = 8.0f;  // log2 units
 
-__device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
+constexpr int BN = 64;                // keys per tile
+constexpr float kLazyRescale = 8.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -72,25 +63,30 @@ struct Tile {
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = D * VROW;
     static constexpr int BUF = KBYTES + VBYTES;  // bytes per buffer
-    static constexpr int BYTES = NS * BUF;
     static constexpr int KINSTR = KBYTES / 1024;  // 1 KiB per wave-wide direct load
     static constexpr int VINSTR = VBYTES / 1024;
     static constexpr int KROWS_PER_INSTR = 1024 / KROW;
     static constexpr int VROWS_PER_INSTR = 1024 / VROW;
     static_assert(KINSTR % NW == 0 && VINSTR % NW == 0, "tile loads must split evenly over the waves");
-    static constexpr int LOADS_PER_WAVE = KINSTR / NW + VINSTR / NW;
-    static_assert(LOADS_PER_WAVE < 16, "vmcnt immediate");
-    // wait until at most n tiles' loads (the newest) are still in flight
-    __device__ static __forceinline__ void wait_tiles_in_flight(int n) {
-        if (n <= 0)
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        else if (n == 1)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_WAVE);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS_PER_WAVE));
-    }
 
     __device__ static __forceinline__ int kswz(int r, int c) { return D == 128 ? swz256(r, c) : swz128(r, c); }
+
+    // Operand-read addresses. For a lane reading row r (K) or d-row r (V^T),
+    // the physical chunk is (logical chunk) ^ key(r) with key depending only
+    // on r mod 16, and the XORed bits (5..7) are disjoint from the row and
+    // buffer bits. So every read address of a tile is a per-lane base plus
+    // the buffer offset, XORed with a constant, plus an immediate offset:
+    //   K   row 32 tt + l32, chunk 2 j + hf:  ((A0 + buf) ^ 32 j) + tt * 32 * KROW
+    //   V^T row 32 c + l32,  chunk 4 tt + 2 g + hf:  ((B0 + buf) ^ (64 tt + 32 g)) + c * 32 * VROW
+    // A0 and B0 are the only per-lane address registers kept live.
+    __device__ static __forceinline__ uint32_t kbase(int l32, int hf) {
+        const int key = D == 128 ? (l32 & 15) : swz128(l32, 0);
+        return (uint32_t)(l32 * KROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
+    }
+    __device__ static __forceinline__ uint32_t vbase(int l32, int hf) {
+        const int key = swz128(l32, 0);
+        return (uint32_t)(KBYTES + l32 * VROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
+    }
     // byte offset of logical chunk c of K row r / V^T row r inside a buffer
     __device__ static __forceinline__ int koff(int r, int c) { return r * KROW + kswz(r, c) * 16; }
     __device__ static __forceinline__ int voff(int r, int c) { return KBYTES + r * VROW + swz128(r, c) * 16; }
@@ -123,7 +119,8 @@ struct Tile {
     // Issue this wave's share of the direct global->LDS loads of one K/V^T
     // tile: a wave-uniform tile base plus the loop-invariant lane offsets. The
     // packed capacity is a multiple of the tile, so the last tile never leaves
-    // the allocation; its rows past nk are masked (K) or zeroed (V^T) after.
+    // the allocation; its rows past nk hold zeros written by the pack step,
+    // and their scores are masked.
     __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, const unsigned char *kb,
                                                  const unsigned char *vb, int64_t k0, int w) {
         const unsigned char *kt = kb + k0 * KROW;
@@ -138,19 +135,6 @@ struct Tile {
                                              (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024), 16, 0, 0);
     }
 
-    // Zero the V^T entries of keys >= nk in the last tile (P is 0 there, but the
-    // packed rows past nk are not written by the pack and may hold non-finite
-    // bits).
-    __device__ static __forceinline__ void zero_tail(unsigned char *buf, int64_t k0, int64_t nk, int t) {
-        for (int e = t; e < D * BN; e += NW * 64) {
-            const int r = e / BN, sc = e % BN;  // d-row, stored column
-            const int64_t key = k0 + (sc & ~15) + group_perm(sc & 15);
-            if (key >= nk) {
-                bf16 *q = reinterpret_cast<bf16 *>(buf + voff(r, sc >> 3)) + (sc & 7);
-                *q = (bf16)0.0f;
-            }
-        }
-    }
 };
 
 __device__ __forceinline__ void vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -163,12 +147,13 @@ __device__ __forceinline__ float half_swap_partner(float x) {
     return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
 }
 
-template <int D, int NW, int U, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+template <int D, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int BM = NW * U * 32;  // queries per workgroup
-    constexpr int DC = D / 16;       // k-steps of Q.K^T
-    constexpr int DT = D / 32;       // 32-row d tiles of O^T
+    constexpr int BM = NW * 32;  // queries per workgroup (32 per wave)
+    constexpr int DC = D / 16;   // k-steps of Q.K^T
+    constexpr int DT = D / 32;   // 32-row d tiles of O^T
+    constexpr int NSTAGE = 3;    // tiles resident or in flight in LDS
     typedef Tile<D, NW> T;
     extern __shared__ __align__(1024) unsigned char smem[];
 
@@ -189,16 +174,14 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int lane = t & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
-    const int64_t q_base = (int64_t)qt * BM + w * (32 * U);
+    const int64_t q_row = (int64_t)qt * BM + w * 32 + l32;
 
     // ---- Q load: rotate in fp32, scale by scale*log2(e), one bf16 rounding ----
-    bf16x8 qreg[U][DC];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t row = q_base + 32 * u + l32;
-        const bool valid = row < a.nq;
-        const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + row * a.q_rs + (int64_t)head * a.q_hs;
-        const float *tb = a.q_rope ? a.q_rope + row * D : nullptr;  // [row][D/2][2]
+    bf16x8 qreg[DC];
+    {
+        const bool valid = q_row < a.nq;
+        const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + q_row * a.q_rs + (int64_t)head * a.q_hs;
+        const float *tb = a.q_rope ? a.q_rope + q_row * D : nullptr;  // [row][D/2][2]
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
             const int dcol = 16 * j + 8 * hf;
@@ -223,247 +206,254 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = (bf16)(xf[e] * a.scale_log2);
             }
-            qreg[u][j] = x;
+            qreg[j] = x;
         }
     }
 
-    f32x16 o[DT][U];
+    f32x16 o[DT];
 #pragma unroll
-    for (int c = 0; c < DT; ++c)
-#pragma unroll
-        for (int u = 0; u < U; ++u) o[c][u] = f32x16{};
-    float l[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) l[u] = 0.f;
+    for (int c = 0; c < DT; ++c) o[c] = f32x16{};
+    float l = 0.f;
 
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)head * a.cap * D * 2;
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(a.v) + (int64_t)head * D * a.cap * 2;
     const int ntiles = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
-
-    // NS-stage K/V pipeline: tiles kt+1 .. kt+NS-1 are in flight while tile kt
-    // is used.
-    for (int p = 0; p < NS - 1 && p < ntiles; ++p)
-        T::issue(smem + p * T::BUF, T::plan(a.cap, wu, lane), kb, vb, (int64_t)p * BN, wu);
-    T::wait_tiles_in_flight(min(NS - 2, ntiles - 1));
-    __syncthreads();
-
-    // Running max m (log2 units, per query). The hot variant keeps m = 0 and
-    // seeds the score accumulator with the constant 0: it is exact as long as
-    // every tile max stays below 2^8 (and the first tile's above 2^-8), which
-    // bounds P by 256 and keeps the sum far from under/overflow. A wave that
-    // sees a tile outside that band returns false before touching P and
-    // redoes that tile, and the rest, in the cold variant, which carries m
-    // explicitly and rescales O and l when it must rise. Keeping the O
-    // rescale out of the hot variant keeps a second copy of the O
-    // accumulators out of its live set. Both variants meet exactly one
-    // end-of-tile barrier per tile; `redo` skips the tile's load issue and
-    // the last tile's zeroing barrier that the hot variant already passed.
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    const f32x16 zero16 = f32x16{};
+    const uint32_t A0 = T::kbase(l32, hf);
+    const uint32_t B0 = T::vbase(l32, hf);
 
-    // m / negm: running max and its negation broadcast over an accumulator
-    // (cold variant only; the hot variant never touches them, so they are not
-    // live across the hot loop).
-    auto body = [&](auto hot_tag, const int kt, unsigned char *buf, unsigned char *nbuf, const bool redo,
-                    float *m, f32x16 *negm) __attribute__((always_inline)) -> bool {
-        constexpr bool HOT = decltype(hot_tag)::value;
-        // Per-lane LDS and global offsets are recomputed from an opaque copy of
-        // the lane id every tile (a dozen VALU ops) instead of being hoisted
-        // out of the loop, where they would crowd the register file.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int l32 = ln & 31, hf = ln >> 5;
-        if (ragged && kt + 1 == ntiles && !redo) {
-            T::zero_tail(buf, (int64_t)kt * BN, a.nk, t);
-            __syncthreads();
-        }
-        if (kt + NS - 1 < ntiles && !redo)
-            T::issue(nbuf, T::plan(a.cap, wu, ln), kb, vb, (int64_t)(kt + NS - 1) * BN, wu);
+    // Every tile follows one schedule on every path: at tile kt a wave issues
+    // its share of tile kt+2's direct loads, computes, waits for its own loads
+    // (vmcnt 0) and meets one workgroup barrier. So at each barrier every
+    // wave's share of the tile two ahead has landed, and a buffer is refilled
+    // only after every wave has passed the barrier that ends its last use.
+    auto buf_of = [&](int kt) __attribute__((always_inline)) { return smem + (kt % NSTAGE) * T::BUF; };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), kb, vb, (int64_t)kt * BN, wu);
+    };
+    auto end_tile = [&]() __attribute__((always_inline)) {
+        vmcnt0();
+        __syncthreads();
+    };
 
-        // ---- S^T (log2 units, minus m) = K Q^T + (-m) ----------------------
-        f32x16 s[2][U];
-        bf16x8 ka0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, hf));
-        bf16x8 ka1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, hf));
+    // S^T (log2 units) minus the seed: K Q^T + seed, for the tile in buf.
+    auto qk = [&](const unsigned char *buf, f32x16 (&s)[2], const f32x16 &seed) __attribute__((always_inline)) {
+        const uint32_t kb0 = (uint32_t)(buf - smem) + A0;
+        auto kread = [&](int j, int tt) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(smem + ((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW));
+        };
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
-            bf16x8 kn0, kn1;
-            if (SA_FWD_PREFETCH && j + 1 < DC) {
-                kn0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, 2 * (j + 1) + hf));
-                kn1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, 2 * (j + 1) + hf));
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const f32x16 c0 = j ? s[0][u] : (HOT ? f32x16{} : negm[u]);
-                const f32x16 c1 = j ? s[1][u] : (HOT ? f32x16{} : negm[u]);
-                s[0][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[u][j], c0, 0, 0, 0);
-                s[1][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[u][j], c1, 0, 0, 0);
-            }
-            if (SA_FWD_PREFETCH && j + 1 < DC) {
-                ka0 = kn0;
-                ka1 = kn1;
-            } else if (j + 1 < DC) {
-                ka0 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(l32, 2 * (j + 1) + hf));
-                ka1 = *reinterpret_cast<const bf16x8 *>(buf + T::koff(32 + l32, 2 * (j + 1) + hf));
-            }
+            const bf16x8 ka0 = kread(j, 0), ka1 = kread(j, 1);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[j], j ? s[0] : seed, 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[j], j ? s[1] : seed, 0, 0, 0);
         }
-
-        // ---- mask keys >= nk (last tile only) --------------------------------
+    };
+    // Keys >= nk of the last tile get -inf scores.
+    auto mask = [&](f32x16 (&s)[2], int kt) __attribute__((always_inline)) {
         if (ragged && kt + 1 == ntiles) {
             // key (tile-relative) = 32 tt + 8 (i / 4) + 4 hf + i % 4 is masked when >= nk - k0
             const int lim = (int)(a.nk - (int64_t)kt * BN) - 4 * hf;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (32 * tt + 8 * (i >> 2) + (i & 3) >= lim) {
+                for (int i = 0; i < 16; ++i)
+                    if (32 * tt + 8 * (i >> 2) + (i & 3) >= lim) s[tt][i] = -__builtin_inff();
+        }
+    };
+    auto tile_max = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+        float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-                        for (int u = 0; u < U; ++u) s[tt][u][i] = -__builtin_inff();
-                    }
+        for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+        return fmaxf(mx, half_swap_partner(mx));  // both half-waves hold the same query
+    };
+    // For each 16-key group (tt, g): P = 2^s rounded to bf16 (already in the
+    // B-operand layout of O^T += V^T P^T), l += the sum of those bf16 values,
+    // then the four d-tiles' products with that group. The next group's
+    // exponentials overlap this group's matrix-core work.
+    auto exp_pv = [&](const unsigned char *buf, const f32x16 (&s)[2], const float m) __attribute__((always_inline)) {
+        const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
+        auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(smem + ((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW));
+        };
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                bf16x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    bf16x2 pp;
+                    pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e] - m);
+                    pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e + 1] - m);
+                    ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
+                    pv[e] = pp.x;
+                    pv[e + 1] = pp.y;
                 }
-        }
-
-#if SA_FWD_EARLY_V
-        // first V^T operand, read while the softmax runs
-        bf16x8 va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(l32, hf));
-#endif
-
-        // ---- online softmax ---------------------------------------------------
-        bf16x8 pb[2][2][U];  // [key subtile][16-key group][query subtile]
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float mx = s[0][u][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][u][i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][u][i]);
-            mx = fmaxf(mx, half_swap_partner(mx));  // tile max of s - m for this query
-            if (HOT) {
-                if (__any(mx > kLazyRescale || (kt == 0 && mx < -kLazyRescale))) return false;
-            } else if (kt == 0) {
-                // no accumulation yet: a lane outside the band adopts its first
-                // tile's max; the others keep m = 0 and match the hot variant
-                // bit for bit
-                const float delta = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
-                m[u] = delta;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) s[tt][u] -= delta;
-                negm[u] = -delta;
-            } else if (__any(mx > kLazyRescale)) {
-                const float delta = mx > kLazyRescale ? mx : 0.0f;
-                const float alpha = __builtin_amdgcn_exp2f(-delta);
-                l[u] *= alpha;
-#pragma unroll
-                for (int c = 0; c < DT; ++c) o[c][u] *= alpha;
-                m[u] += delta;
-                negm[u] = -m[u];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) s[tt][u] -= delta;
+                for (int c = 0; c < DT; ++c)
+                    o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(c, tt, g), pv, o[c], 0, 0, 0);
             }
-            float ls[2] = {0.f, 0.f};
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    bf16x8 pv;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        bf16x2 pp;
-                        pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][u][8 * g + e]);
-                        pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][u][8 * g + e + 1]);
-                        ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
-                        pv[e] = pp.x;
-                        pv[e + 1] = pp.y;
-                    }
-                    pb[tt][g][u] = pv;
-                }
-            l[u] += ls[0] + ls[1];
-        }
-
-        // ---- O^T += V^T P^T ---------------------------------------------------
-#if !SA_FWD_EARLY_V
-        bf16x8 va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(l32, hf));
-#endif
-#pragma unroll
-        for (int idx = 0; idx < DT * 4; ++idx) {
-            const int c = idx >> 2, tt = (idx >> 1) & 1, g = idx & 1;
-            bf16x8 vn;
-            if (SA_FWD_PREFETCH && idx + 1 < DT * 4) {
-                const int c2 = (idx + 1) >> 2, tt2 = ((idx + 1) >> 1) & 1, g2 = (idx + 1) & 1;
-                vn = *reinterpret_cast<const bf16x8 *>(buf + T::voff(32 * c2 + l32, 4 * tt2 + 2 * g2 + hf));
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                o[c][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tt][g][u], o[c][u], 0, 0, 0);
-            if (SA_FWD_PREFETCH && idx + 1 < DT * 4) {
-                va = vn;
-            } else if (idx + 1 < DT * 4) {
-                const int c2 = (idx + 1) >> 2, tt2 = ((idx + 1) >> 1) & 1, g2 = (idx + 1) & 1;
-                va = *reinterpret_cast<const bf16x8 *>(buf + T::voff(32 * c2 + l32, 4 * tt2 + 2 * g2 + hf));
-            }
-        }
-
-        // the next tile's loads have landed (later tiles may still be in flight)
-        T::wait_tiles_in_flight(min(NS - 2, ntiles - 2 - kt));
-        __syncthreads();
-        return true;
+        l += ls[0] + ls[1];
     };
 
-    typedef std::integral_constant<bool, true> Hot;
-    typedef std::integral_constant<bool, false> Cold;
-    constexpr int SB = T::BUF;
-    int kt = 0;
-#if SA_FWD_UNROLL_STAGES
-    bool left_hot = false;
-    for (; kt < ntiles && !left_hot; kt += NS) {
+    // Hot-loop block, scheduled by hand: the scores of the next tile (QK) and
+    // the softmax + P.V of this tile, in four 16-key groups. Each group first
+    // issues its four V^T operand reads, then runs two k-steps of the next
+    // tile's Q.K^T (K operands read two steps ahead) interleaved with its
+    // exponentials, then its four P.V products. Every operand read is issued
+    // several matrix-core ops before its use, so LDS latency stays hidden;
+    // sched_barrier pins the order.
+    auto qk_exp_pv = [&](const unsigned char *nbuf, f32x16 (&sn)[2], const unsigned char *buf,
+                         const f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const uint32_t kb0 = (uint32_t)(nbuf - smem) + A0;
+        const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
+        auto kread = [&](int j, int tt) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(smem + ((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW));
+        };
+        auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(smem + ((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW));
+        };
+        constexpr int KSTEPS_PER_GROUP = DC / 4;
+        bf16x8 kr[DC][2];
+        kr[0][0] = kread(0, 0);
+        kr[0][1] = kread(0, 1);
+        if (DC > 1) {
+            kr[1][0] = kread(1, 0);
+            kr[1][1] = kread(1, 1);
+        }
+        float ls[2] = {0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            if (kt + i < ntiles &&
-                !body(Hot(), kt + i, smem + i * SB, smem + ((i + NS - 1) % NS) * SB, false, nullptr, nullptr)) {
-                kt += i;
-                left_hot = true;
-                break;
+        for (int grp = 0; grp < 4; ++grp) {
+            const int tt = grp >> 1, g = grp & 1;
+            bf16x8 vr[DT];
+#pragma unroll
+            for (int c = 0; c < DT; ++c) vr[c] = vread(c, tt, g);
+            bf16x8 pv;
+#pragma unroll
+            for (int h = 0; h < KSTEPS_PER_GROUP; ++h) {
+                const int j = grp * KSTEPS_PER_GROUP + h;
+                if (j + 2 < DC) {
+                    kr[j + 2][0] = kread(j + 2, 0);
+                    kr[j + 2][1] = kread(j + 2, 1);
+                }
+                sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][0], qreg[j], j ? sn[0] : zero16, 0, 0, 0);
+                sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][1], qreg[j], j ? sn[1] : zero16, 0, 0, 0);
+                // this k-step's share of the group's exponentials
+                constexpr int E = 8 / KSTEPS_PER_GROUP;
+#pragma unroll
+                for (int e = h * E; e < (h + 1) * E; e += 2) {
+                    bf16x2 pp;
+                    pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e]);
+                    pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e + 1]);
+                    ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
+                    pv[e] = pp.x;
+                    pv[e + 1] = pp.y;
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-    }
-    if (left_hot) kt -= NS;  // undo the loop increment taken on exit
-#else
-    for (int st = 0; kt < ntiles; ++kt, st = (st + 1 == NS ? 0 : st + 1)) {
-        const int nst = st == 0 ? NS - 1 : st - 1;  // stage of tile kt + NS - 1
-        if (!body(Hot(), kt, smem + st * SB, smem + nst * SB, false, nullptr, nullptr)) break;
-    }
-#endif
-    // Cold path (rare): redo the tile that left the hot band, then finish. The
-    // hot variant kept m = 0, so the cold variant starts from there.
-    if (kt < ntiles) {
-        float m[U];
-        f32x16 negm[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            m[u] = 0.f;
-            negm[u] = f32x16{};
+            for (int c = 0; c < DT; ++c) o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c], pv, o[c], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        for (bool redo = true; kt < ntiles; ++kt, redo = false)
-            body(Cold(), kt, smem + (kt % NS) * SB, smem + ((kt + NS - 1) % NS) * SB, redo, m, negm);
+        l += ls[0] + ls[1];
+    };
+
+    issue(0);
+    issue(1);
+    end_tile();
+
+    // ---- hot loop: running max anchored at 0, software-pipelined ----------
+    // The running max m stays 0 and the score accumulator is seeded with the
+    // constant 0; this is exact while every tile's max stays below 2^8 (and
+    // the first tile's above 2^-8), which bounds P by 256 and keeps the sum far
+    // from under/overflow. While the softmax of tile kt runs on the VALU, the
+    // matrix cores already compute the scores of tile kt+1. A wave that sees a
+    // tile outside the band leaves before touching P and finishes in the cold
+    // loop below, which carries m explicitly and rescales O and l when it must
+    // rise (keeping that rescale out of this loop keeps a second copy of the O
+    // accumulators out of its live set).
+    f32x16 s[2];
+    qk(buf_of(0), s, zero16);
+    int kt = 0;
+    for (; kt < ntiles; ++kt) {
+        issue(kt + 2);
+        mask(s, kt);
+        const float mx = tile_max(s);
+        if (__any(mx > kLazyRescale || (kt == 0 && mx < -kLazyRescale))) break;
+        // Scores of the next tile and the softmax + P.V of this one sit in one
+        // basic block so the scheduler can interleave matrix-core and VALU
+        // work. On the last tile the next-tile scores read a resident buffer
+        // and are discarded.
+        f32x16 sn[2];
+#if SA_FWD_HAND
+        qk_exp_pv(buf_of(kt + 1), sn, buf_of(kt), s);
+#else
+        qk(buf_of(kt + 1), sn, zero16);
+        exp_pv(buf_of(kt), s, 0.0f);
+#endif
+#if SA_FWD_SGB
+        // interleave: each matrix-core op followed by one LDS read and a few VALU ops
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, SA_FWD_SGB, 0);  // VALU
+        }
+#endif
+        s[0] = sn[0];
+        s[1] = sn[1];
+        end_tile();
+    }
+
+    // ---- cold loop (rare): explicit running max, not pipelined ---------------
+    // Scores are formed exactly as in the hot loop (seed 0) and m is
+    // subtracted in the exponent. O and l are rescaled on every tile, by
+    // exactly 1 where m does not move, so there is no branch around the
+    // rescale; a lane whose max stays in the band keeps m = 0 and computes
+    // bit for bit what the hot loop would have.
+    if (kt < ntiles) {
+        float m = 0.f;  // the hot loop kept m = 0
+        for (bool redo = true; kt < ntiles; ++kt, redo = false) {
+            if (!redo) issue(kt + 2);  // the hot loop already issued it for the redone tile
+            qk(buf_of(kt), s, zero16);
+            mask(s, kt);
+            const float mx = tile_max(s);  // absolute tile max (log2 units)
+            float mnew;
+            if (kt == 0)  // nothing accumulated yet: adopt the first tile's max if out of band
+                mnew = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
+            else
+                mnew = (mx - m > kLazyRescale) ? mx : m;
+            const float alpha = kt == 0 ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
+#pragma unroll
+            for (int c = 0; c < DT; ++c) o[c] *= alpha;
+            m = mnew;
+            exp_pv(buf_of(kt), s, m);
+            end_tile();
+        }
     }
 
     // ---- epilogue: O / l, store ----------------------------------------------
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const float lt = l[u] + half_swap_partner(l[u]);
-        const float inv = 1.0f / lt;
-        const int64_t row = q_base + 32 * u + l32;
-        if (row >= a.nq) continue;
-        const int64_t obase = row * a.o_rs + (int64_t)head * a.o_hs;
+    const float lt = l + half_swap_partner(l);
+    const float inv = 1.0f / lt;
+    if (q_row < a.nq) {
+        const int64_t obase = q_row * a.o_rs + (int64_t)head * a.o_hs;
 #pragma unroll
         for (int c = 0; c < DT; ++c)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = 32 * c + 8 * g + 4 * hf;
                 f32x4 r;
-                r.x = o[c][u][4 * g + 0] * inv;
-                r.y = o[c][u][4 * g + 1] * inv;
-                r.z = o[c][u][4 * g + 2] * inv;
-                r.w = o[c][u][4 * g + 3] * inv;
+                r.x = o[c][4 * g + 0] * inv;
+                r.y = o[c][4 * g + 1] * inv;
+                r.z = o[c][4 * g + 2] * inv;
+                r.w = o[c][4 * g + 3] * inv;
                 if (OUT_F32) {
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + obase + d0) = r;
                 } else {
@@ -481,19 +471,15 @@ void fwd_bf16_kernel(FwdArgs a) {
 #ifndef SA_FWD_WAVES
 #define SA_FWD_WAVES 8
 #endif
-#ifndef SA_FWD_SUBTILES
-#define SA_FWD_SUBTILES 1
-#endif
 constexpr int kNW = SA_FWD_WAVES;
-constexpr int kU = SA_FWD_SUBTILES;
 
 template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
-    constexpr int BM = kNW * kU * 32;
+    constexpr int BM = kNW * 32;
     const int64_t n_qt = (a.nq + BM - 1) / BM;
     const int64_t nwg = n_qt * a.heads;
-    auto kern = fwd_bf16_kernel<D, kNW, kU, OUT_F32>;
-    constexpr int lds_bytes = Tile<D, kNW>::BYTES;
+    auto kern = fwd_bf16_kernel<D, kNW, OUT_F32>;
+    constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,
     // idempotent, no stream work).
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -504,6 +490,8 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int fwd_bf16_rows_per_workgroup() { return kNW * 32; }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream) {
     if (a.nq == 0) return hipSuccess;

@@ -14,7 +14,7 @@ namespace sa {
 
 namespace {
 
-constexpr int kQ = 64;         // queries per workgroup
+constexpr int kQ = kFwdF32RowsPerWorkgroup;  // queries per workgroup
 constexpr int kThreads = 128;  // two lanes per query
 constexpr int kTN = 32;        // keys per tile
 

@@ -156,7 +156,48 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
     }
 }
 
+// Zero the padding rows [rows, pad_end) of every head: the forward pass reads
+// whole 64-row tiles and multiplies the values of masked keys by P = 0, which
+// must meet finite numbers. bf16: K rows and the V^T stored columns that hold
+// those rows; f32: K and V rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void zero_pad_kernel(PackArgs a, int64_t rows, int64_t pad_end, int is_bf16) {
+    const int h = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t n = pad_end - rows;
+    if (is_bf16) {
+        bf16 *kp = reinterpret_cast<bf16 *>(a.k_packed) + (int64_t)h * a.cap * D;
+        bf16 *vp = reinterpret_cast<bf16 *>(a.v_packed) + (int64_t)h * D * a.cap;
+        for (int64_t e = t; e < n * D; e += kThreads) kp[(rows + e / D) * D + e % D] = (bf16)0.0f;
+        const int64_t c0 = rows & ~int64_t(15);  // first stored column of the first partial group
+        const int64_t ncol = pad_end - c0;
+        for (int64_t e = t; e < ncol * D; e += kThreads) {
+            const int64_t col = c0 + e % ncol, dd = e / ncol;
+            const int64_t row = (col & ~int64_t(15)) + group_perm((int)(col & 15));
+            if (row >= rows) vp[dd * a.cap + col] = (bf16)0.0f;
+        }
+    } else {
+        float *kp = reinterpret_cast<float *>(a.k_packed) + (int64_t)h * a.cap * D;
+        float *vp = reinterpret_cast<float *>(a.v_packed) + (int64_t)h * a.cap * D;
+        for (int64_t e = t; e < n * D; e += kThreads) {
+            kp[rows * D + e] = 0.0f;
+            vp[rows * D + e] = 0.0f;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_zero_pad(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t rows, int64_t pad_end,
+                           hipStream_t stream) {
+    if (pad_end <= rows) return hipSuccess;
+    const int bf = dtype == SA_BF16;
+    if (head_dim == 128)
+        hipLaunchKernelGGL(zero_pad_kernel<128>, dim3((unsigned)a.heads), dim3(kThreads), 0, stream, a, rows, pad_end, bf);
+    else
+        hipLaunchKernelGGL(zero_pad_kernel<64>, dim3((unsigned)a.heads), dim3(kThreads), 0, stream, a, rows, pad_end, bf);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream) {
     if (a.n_segs == 0 || max_tiles == 0) return hipSuccess;

@@ -48,6 +48,8 @@ struct PackArgs {
 };
 constexpr int kPackTileRows = 64;  // packed rows per pack workgroup
 hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream);
+hipError_t launch_zero_pad(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t rows, int64_t pad_end,
+                           hipStream_t stream);
 
 // --- forward --------------------------------------------------------------
 struct FwdArgs {
@@ -64,6 +66,8 @@ struct FwdArgs {
     float scale_log2;  // softmax scale * log2(e)
 };
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream);
+int fwd_bf16_rows_per_workgroup();  // query rows one bf16 forward workgroup owns
+constexpr int kFwdF32RowsPerWorkgroup = 64;
 hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t stream);
 
 }  // namespace sa

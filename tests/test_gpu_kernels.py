@@ -41,6 +41,9 @@ def _pack_case(dtype, d=128, heads=3):
     w = I.custom("pack", 200, dtype, heads, d, [37, 64, 100], 10, prompt_rows=19)
     from streaming_video_diffusion_amd.stream import ChunkAttention
     ca = ChunkAttention(w)
+    # one spare tile of capacity so rows past the padding can be checked
+    ca.ctx = B.PackedContext(w.heads, w.head_dim, ca.dtype, w.nk + 64, device="cuda")
+    ca.ctx.rows = w.nk
     ca.ctx.k_packed.fill_(float("nan"))
     ca.ctx.v_packed.fill_(float("nan"))
     ca.pack_static()
@@ -67,15 +70,24 @@ def test_pack_bf16_layout_and_rotation(d):
             assert np.array_equal(got, ref), "prompt keys must be copied exactly"
         assert np.array_equal(vp[row:row + s.rows], v), f"{s.name}: V must be copied bit-exactly"
         row += s.rows
-    # rows past ctx.rows (up to capacity) are never written
-    tail = ca.ctx.k_packed.view(H, cap, d)[:, w.nk:]
-    assert torch.isnan(tail.float()).all()
+    # padding rows [nk, next multiple of 64) are zeroed; rows past them are never written
+    pad_end = (w.nk + 63) // 64 * 64
+    assert torch.equal(ca.ctx.k_packed.view(H, cap, d)[:, w.nk:pad_end].float(),
+                       torch.zeros((H, pad_end - w.nk, d), device="cuda"))
+    vt = ca.ctx.v_packed.view(H, d, cap)
+    cols = [16 * (r // 16) + perm16(r % 16) for r in range(w.nk, pad_end)]
+    assert torch.equal(vt[:, :, cols].float(), torch.zeros((H, d, len(cols)), device="cuda"))
+    assert torch.isnan(ca.ctx.k_packed.view(H, cap, d)[:, pad_end:].float()).all()
 
 
 def test_pack_f32_layout_and_rotation():
     note("[gpu] pack f32")
     w, ca = _pack_case("f32")
     cap, H, d = ca.ctx.capacity_rows, w.heads, w.head_dim
+    pad_end = (w.nk + 63) // 64 * 64
+    for buf in (ca.ctx.k_packed, ca.ctx.v_packed):
+        assert torch.equal(buf.view(H, cap, d)[:, w.nk:pad_end], torch.zeros((H, pad_end - w.nk, d), device="cuda"))
+        assert torch.isnan(buf.view(H, cap, d)[:, pad_end:]).all()
     kp = ca.ctx.k_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy().astype(np.float64)
     vp = ca.ctx.v_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy()
     _, _, segs = ca.host_inputs()

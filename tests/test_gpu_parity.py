@@ -93,3 +93,42 @@ def test_full_size_sampled_rows(make):
         assert np.isfinite(out).all()
         del ca
         torch.cuda.empty_cache()
+
+
+# The kernel's fast path keeps the running max at 0 and is exact while every
+# tile's max (log2 units) stays within +-8 of it; these cases leave that band
+# and run the rescaling path. Unrotated bf16 inputs and a softmax scale of
+# 2^k * ln 2 keep the scores exact on the GPU (the query pre-scale is then
+# exactly 2^k), so the comparison stays within the bf16 bounds.
+@pytest.mark.parametrize("c_log2", [0.5, 4.0], ids=["scale_x0.5", "scale_x4"])
+def test_rescaling_path_large_scores(c_log2):
+    import math
+    w = I.custom(f"peaked{c_log2}", 400 + int(c_log2 * 10), "bf16", 3, 128, [150, 333], 300, rotary=False,
+                 prompt_rows=40, scale=float(np.float32(c_log2 * math.log(2.0))))
+    ca, out = run(w)
+    rel, mx = assert_parity(out, oracle(ca), "bf16", w.name)
+    note(f"  {w.name}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
+
+
+def test_rescaling_path_negative_first_tile():
+    """The first key tile scores far below 0 for every query; later tiles do not."""
+    import math
+    from oracle import attn64
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    w = I.custom("negfirst", 410, "bf16", 2, 128, [64, 200], 150, rotary=False,
+                 scale=float(np.float32(0.5 * math.log(2.0))))
+    q = w.q()
+    segs = [w.kv(i) for i in range(len(w.segments))]
+    qdir = q[:1]
+    q = I.round_bf16(qdir + 0.05 * q)                       # every query close to qdir
+    k0 = I.round_bf16(np.broadcast_to(-3.0 * qdir, segs[0][0].shape))  # first tile: scores ~ -3 |q|^2
+    segs = [(k0, segs[0][1], None), (segs[1][0], segs[1][1], None)]
+    ca = ChunkAttention(w)
+    ca.q.copy_(torch.from_numpy(q).to(torch.bfloat16))
+    ca.segs[0]["k"].copy_(torch.from_numpy(np.ascontiguousarray(k0)).to(torch.bfloat16))
+    note("[gpu] negative first tile")
+    ca.pack_static()
+    out = ca.step().float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    ref = attn64.chunk_attention(q, None, segs, w.axis_dims, w.theta, w.scale)
+    assert_parity(out, ref, "bf16", "negative first tile")
