@@ -24,6 +24,20 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s + ms/chunk at 1344x768 (12096 q x 28480 kv, 40 heads)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (published)
+FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf16.hip")
+FWD_KERNEL = "fwd_bf16_kernel<128, 8, false>"
+# HBM traffic of one forward launch at 1344x768, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch; profiles/fwd_bf16_1344x768_hbm_traffic.txt),
+# each scaled by what the same counter reads for a plain device copy of known
+# size (FETCH_SIZE counts 0.5x the bytes read, WRITE_SIZE 1.0x the bytes
+# written). Valid only for the forward source these counters were taken on.
+TRAFFIC = {
+    "source_sha256": "91e630ecc9e3c3d67a6e7ac252de93993e781020c4001ae8450371ce11cf9b82",
+    "fetch_kib": 2034816.8,
+    "write_kib": 120961.0,
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+}
 
 
 def parse():
@@ -32,8 +46,10 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="full_1344x768")
-    p.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    p.add_argument("--cpu-rows", type=int, default=2560, help="query rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-shard", action="store_true",
+                   help="skip the extra measurement of one GPU's head shard (40/8 = 5 heads)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (3 times) and exit; "
                         "its FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -89,6 +105,45 @@ def cpu_baseline(w, rows_n):
         "host_cpus": os.cpu_count(),
         "affinity": len(os.sched_getaffinity(0)),
     }
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the stored counters, or None when
+    the forward kernel's source has changed since they were taken."""
+    import hashlib
+    if TRAFFIC["source_sha256"] is None:
+        return None
+    with open(FWD_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["source_sha256"]:
+            return None
+    return (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024.0
+
+
+def shard_measure(steps):
+    """Forward pass on one GPU's share of an 8-way head split (5 of 40 heads)
+    at the full 1344x768 shape: an extra line, not the metric."""
+    import torch
+    from streaming_video_diffusion_amd import inputs as I
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    import dataclasses
+    w = dataclasses.replace(I.full_1344x768(), name="full_1344x768_h5", heads=5)
+    ca = ChunkAttention(w, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ca.pack_static(stream)
+    ca.step(stream)
+    for _ in range(3):
+        ca.forward(stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        ca.forward(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"heads": 5, "nq": w.nq, "nk": w.nk, "forward_ms": ms,
+            "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12,
+            "workgroups": ((w.nq + 255) // 256) * w.heads}
 
 
 def main():
@@ -176,14 +231,16 @@ def main():
         "pack_tables_ms_avg": sum(pack_ms) / len(pack_ms),
         "roofline": {
             "bound": "mfma" if bf16 else "alu",
-            "kernel": "fwd_bf16_kernel<128>" if bf16 else "fwd_f32_kernel",
+            "kernel": FWD_KERNEL if bf16 else "fwd_f32_kernel",
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic() if (bf16 and w.name == "full_1344x768") else None,
         },
     }
+    if not args.no_shard:
+        out["one_gpu_head_shard"] = shard_measure(20)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
