@@ -7,26 +7,28 @@
 // page, streaming-context section). K arrives already rotated by the pack
 // step; the query rotation is fused into the Q load.
 //
-// Work decomposition: a workgroup of NW waves owns NW*U*32 query rows of one
-// head; each wave owns U subtiles of 32 queries.
+// Work decomposition: a workgroup of NW waves owns NW*32 query rows of one
+// head; each wave owns 32 queries, two waves share a SIMD.
 //   * Q is rotated in fp32, multiplied by scale*log2(e), rounded once to
 //     bf16 and kept in registers as the B operand of v_mfma_f32_32x32x16_bf16;
 //   * scores are formed transposed, S^T = K Q^T (A = K tile from LDS), so the
-//     32x32 accumulator puts one query column in each lane: the softmax row
-//     max is an in-lane reduction plus one exchange between half-waves, and
-//     the row sum never leaves the lane until the epilogue;
-//   * the accumulator is seeded with -m (the running max, log2 units), so
-//     the matrix core returns s - m and the exponent needs no extra VALU op;
-//     m is raised lazily, only when a tile's max exceeds it by more than
-//     2^8 (exact up to rounding; it skips almost every O rescale);
+//     32x32 accumulator puts one query column in each lane: a row max is an
+//     in-lane reduction plus one exchange between half-waves, and the row sum
+//     never leaves the lane until the epilogue;
+//   * the main pass holds the softmax anchor at 0 (P = 2^s, log2 units) for
+//     the whole row with no per-tile max: exact as long as nothing over- or
+//     underflows, which one check per row at the end establishes; rows that
+//     fail it (rare) are recomputed by a second pass that tracks the running
+//     max explicitly;
 //   * P^T is rounded to bf16 and is already in the B-operand layout of
 //     O^T += V^T P^T; the row sum accumulates those same bf16 values with
 //     v_dot2 (numerator and denominator see identical weights). The pack step
 //     stores V transposed with a 16-row permutation so the A operand (V^T) is
 //     one 16-byte LDS read per lane;
-//   * K and V^T tiles of 64 keys stream through double-buffered LDS with
-//     direct global->LDS 16-byte loads (no staging registers), XOR-swizzled
-//     so the operand reads are free of bank conflicts;
+//   * K and V^T tiles of 64 keys stream through three LDS stages with direct
+//     global->LDS 16-byte loads (no staging registers), XOR-swizzled so the
+//     operand reads are free of bank conflicts; the scores of tile kt+1 are
+//     formed while the softmax and P.V of tile kt run;
 //   * the workgroup -> (head, query tile) map keeps the workgroups that run
 //     together on one XCD on the same head, so its K/V tiles hit that XCD's L2.
 #include <type_traits>
@@ -230,6 +232,9 @@ void fwd_bf16_kernel(FwdArgs a) {
     // wave's share of the tile two ahead has landed, and a buffer is refilled
     // only after every wave has passed the barrier that ends its last use.
     auto buf_of = [&](int kt) __attribute__((always_inline)) { return smem + (kt % NSTAGE) * T::BUF; };
+    // The lane offsets are recomputed at every issue from an opaque copy of
+    // the lane id: a few VALU ops instead of per-lane 64-bit pointers kept
+    // live across the loop, and the loads keep the SGPR-base form.
     auto issue = [&](int kt) __attribute__((always_inline)) {
         if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), kb, vb, (int64_t)kt * BN, wu);
     };
@@ -311,6 +316,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     // sched_barrier pins the order.
     auto qk_exp_pv = [&](const unsigned char *nbuf, f32x16 (&sn)[2], const unsigned char *buf,
                          const f32x16 (&s)[2]) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
         const uint32_t kb0 = (uint32_t)(nbuf - smem) + A0;
         const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
         auto kread = [&](int j, int tt) __attribute__((always_inline)) {
@@ -364,85 +370,10 @@ void fwd_bf16_kernel(FwdArgs a) {
         l += ls[0] + ls[1];
     };
 
-    issue(0);
-    issue(1);
-    end_tile();
-
-    // ---- hot loop: running max anchored at 0, software-pipelined ----------
-    // The running max m stays 0 and the score accumulator is seeded with the
-    // constant 0; this is exact while every tile's max stays below 2^8 (and
-    // the first tile's above 2^-8), which bounds P by 256 and keeps the sum far
-    // from under/overflow. While the softmax of tile kt runs on the VALU, the
-    // matrix cores already compute the scores of tile kt+1. A wave that sees a
-    // tile outside the band leaves before touching P and finishes in the cold
-    // loop below, which carries m explicitly and rescales O and l when it must
-    // rise (keeping that rescale out of this loop keeps a second copy of the O
-    // accumulators out of its live set).
-    f32x16 s[2];
-    qk(buf_of(0), s, zero16);
-    int kt = 0;
-    for (; kt < ntiles; ++kt) {
-        issue(kt + 2);
-        mask(s, kt);
-        const float mx = tile_max(s);
-        if (__any(mx > kLazyRescale || (kt == 0 && mx < -kLazyRescale))) break;
-        // Scores of the next tile and the softmax + P.V of this one sit in one
-        // basic block so the scheduler can interleave matrix-core and VALU
-        // work. On the last tile the next-tile scores read a resident buffer
-        // and are discarded.
-        f32x16 sn[2];
-#if SA_FWD_HAND
-        qk_exp_pv(buf_of(kt + 1), sn, buf_of(kt), s);
-#else
-        qk(buf_of(kt + 1), sn, zero16);
-        exp_pv(buf_of(kt), s, 0.0f);
-#endif
-#if SA_FWD_SGB
-        // interleave: each matrix-core op followed by one LDS read and a few VALU ops
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, SA_FWD_SGB, 0);  // VALU
-        }
-#endif
-        s[0] = sn[0];
-        s[1] = sn[1];
-        end_tile();
-    }
-
-    // ---- cold loop (rare): explicit running max, not pipelined ---------------
-    // Scores are formed exactly as in the hot loop (seed 0) and m is
-    // subtracted in the exponent. O and l are rescaled on every tile, by
-    // exactly 1 where m does not move, so there is no branch around the
-    // rescale; a lane whose max stays in the band keeps m = 0 and computes
-    // bit for bit what the hot loop would have.
-    if (kt < ntiles) {
-        float m = 0.f;  // the hot loop kept m = 0
-        for (bool redo = true; kt < ntiles; ++kt, redo = false) {
-            if (!redo) issue(kt + 2);  // the hot loop already issued it for the redone tile
-            qk(buf_of(kt), s, zero16);
-            mask(s, kt);
-            const float mx = tile_max(s);  // absolute tile max (log2 units)
-            float mnew;
-            if (kt == 0)  // nothing accumulated yet: adopt the first tile's max if out of band
-                mnew = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
-            else
-                mnew = (mx - m > kLazyRescale) ? mx : m;
-            const float alpha = kt == 0 ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
-            l *= alpha;
-#pragma unroll
-            for (int c = 0; c < DT; ++c) o[c] *= alpha;
-            m = mnew;
-            exp_pv(buf_of(kt), s, m);
-            end_tile();
-        }
-    }
-
-    // ---- epilogue: O / l, store ----------------------------------------------
-    const float lt = l + half_swap_partner(l);
-    const float inv = 1.0f / lt;
-    if (q_row < a.nq) {
+    // Output of this lane's half of row q_row: O^T column l32, d-rows
+    // 32 c + 8 g + 4 hf .. +3 of each 32-row d tile.
+    auto store = [&](float lsum) __attribute__((always_inline)) {
+        const float inv = 1.0f / lsum;
         const int64_t obase = q_row * a.o_rs + (int64_t)head * a.o_hs;
 #pragma unroll
         for (int c = 0; c < DT; ++c)
@@ -465,6 +396,97 @@ void fwd_bf16_kernel(FwdArgs a) {
                     *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.out) + obase + d0) = b;
                 }
             }
+    };
+
+    // ---- main pass: running max held at 0 ----------------------------------
+    // Softmax is invariant to the max it subtracts; holding it at 0 is exact
+    // as long as nothing over- or underflows: P = 2^s stays a normal float for
+    // s in (-126, 128), and the row's result is then the same as with any other
+    // anchor up to rounding. That is checked once per row at the end (row sum
+    // within [2^-100, 2^100], O finite); a row that fails is recomputed by the
+    // second pass below with an explicit running max. While the softmax of tile
+    // kt runs on the VALU, the matrix cores already form the scores of tile
+    // kt+1.
+    issue(0);
+    issue(1);
+    end_tile();
+    f32x16 s[2];
+    qk(buf_of(0), s, zero16);
+    for (int kt = 0; kt < ntiles; ++kt) {
+        // On the last tile the next-tile scores read a resident buffer and are
+        // discarded.
+        issue(kt + 2);
+        mask(s, kt);
+        f32x16 sn[2];
+#if SA_FWD_HAND
+        qk_exp_pv(buf_of(kt + 1), sn, buf_of(kt), s);
+#else
+        qk(buf_of(kt + 1), sn, zero16);
+        exp_pv(buf_of(kt), s, 0.0f);
+#endif
+        s[0] = sn[0];
+        s[1] = sn[1];
+        end_tile();
+    }
+
+    // ---- per-row check and store ----------------------------------------------
+    float lt = l + half_swap_partner(l);
+    float osum = 0.f;  // any inf or NaN in O propagates into the sum
+#pragma unroll
+    for (int c = 0; c < DT; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) osum += o[c][i];
+    osum += half_swap_partner(osum);
+    const bool row = q_row < a.nq;
+    const bool ok = lt >= 0x1p-100f && lt <= 0x1p+100f && __builtin_isfinite(osum);
+    if (row && ok) store(lt);
+
+    // ---- second pass (rare): explicit running max ---------------------------
+    // Taken by the whole workgroup when any of its rows failed the check;
+    // every wave streams the tiles again (one barrier per tile, as in the main
+    // pass), and only failed rows are stored, so a row's output never depends
+    // on its neighbours. Scores are formed as in the main pass and m is
+    // subtracted in the exponent; m is raised when a tile's max exceeds it by
+    // more than 2^8, and O and l are rescaled on every tile (by exactly 1 when
+    // m does not move).
+    // Workgroup vote through LDS: one flag per wave in the third buffer, which
+    // the second pass's first two tile loads do not touch (every wave reads
+    // the flags before the barrier that follows those loads).
+    unsigned *flags = reinterpret_cast<unsigned *>(smem + 2 * T::BUF);
+    const unsigned wave_fail = __any(row && !ok) ? 1u : 0u;  // vote of the whole wave, outside the lane-0 branch
+    if (lane == 0) flags[w] = wave_fail;
+    __syncthreads();
+    unsigned any_fail = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any_fail |= flags[i];
+    if (any_fail) {
+#pragma unroll
+        for (int c = 0; c < DT; ++c) o[c] = f32x16{};
+        l = 0.f;
+        float m = 0.f;
+        issue(0);
+        issue(1);
+        end_tile();
+        for (int kt = 0; kt < ntiles; ++kt) {
+            issue(kt + 2);
+            qk(buf_of(kt), s, zero16);
+            mask(s, kt);
+            const float mx = tile_max(s);  // absolute tile max (log2 units)
+            float mnew;
+            if (kt == 0)  // nothing accumulated yet: adopt the first tile's max if out of band
+                mnew = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
+            else
+                mnew = (mx - m > kLazyRescale) ? mx : m;
+            const float alpha = kt == 0 ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
+#pragma unroll
+            for (int c = 0; c < DT; ++c) o[c] *= alpha;
+            m = mnew;
+            exp_pv(buf_of(kt), s, m);
+            end_tile();
+        }
+        lt = l + half_swap_partner(l);
+        if (row && !ok) store(lt);
     }
 }
 

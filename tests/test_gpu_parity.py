@@ -132,3 +132,66 @@ def test_rescaling_path_negative_first_tile():
     torch.cuda.synchronize()
     ref = attn64.chunk_attention(q, None, segs, w.axis_dims, w.theta, w.scale)
     assert_parity(out, ref, "bf16", "negative first tile")
+
+
+# Rows the main pass cannot hold at a fixed anchor go through the second pass:
+# a row whose every score lies far below the float range of 2^s (its row sum
+# underflows), and rows whose largest scores overflow 2^s, mixed with ordinary
+# rows in the same workgroups.
+def test_second_pass_underflowing_rows():
+    """Every key is close to a direction u; queries -16 u (exact in bf16) score about -260 (log2 units)."""
+    from oracle import attn64
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    w = I.custom("underflow", 411, "bf16", 2, 128, [64, 333], 300, rotary=False, prompt_rows=7)
+    rng = np.random.default_rng(5)
+    u = I.round_bf16(rng.standard_normal((1, w.heads, w.head_dim)).astype(np.float32))
+    q = w.q()
+    q[:40] = -16.0 * u  # rows 0..39: every score far below 2^-126
+    segs = []
+    for i in range(len(w.segments)):
+        k, v = w.kv(i)
+        k = I.round_bf16(u + 0.05 * k)
+        segs.append((k, v, None))
+    ca = ChunkAttention(w)
+    ca.q.copy_(torch.from_numpy(q).to(torch.bfloat16))
+    for s, (k, v, _) in zip(ca.segs, segs):
+        s["k"].copy_(torch.from_numpy(np.ascontiguousarray(k)).to(torch.bfloat16))
+    note("[gpu] second pass: underflowing rows")
+    ca.pack_static()
+    out = ca.step().float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all()
+    ref = attn64.chunk_attention(q, None, segs, w.axis_dims, w.theta, w.scale)
+    rel, mx = assert_parity(out, ref, "bf16", "underflowing rows")
+    note(f"  rel-L2 {rel:.3e} max-abs {mx:.3e}")
+
+
+def test_second_pass_mixed_rows_keep_neighbours_bitwise():
+    """A few query rows scaled by 32 overflow; every row matches the oracle and
+    the other rows are bit-identical to a run without the scaled rows.
+
+    Unrotated inputs and a softmax scale of ln2 / 8 make the query pre-scale
+    exactly 2^-3, so even the scaled rows' scores (up to about 2^7 in log2
+    units) are exact on the GPU and the comparison stays within the bf16
+    bounds; ordinary rows peak near 4.5 and stay in the main pass."""
+    import math
+    w = I.custom("mixed", 412, "bf16", 3, 128, [100, 400, 530], 700, rotary=False, prompt_rows=11,
+                 scale=float(np.float32(math.log(2.0) / 8.0)))
+    ca, base = run(w)
+    a = ca.forward().clone()
+    rows = [3, 257, 258, 511, 699]
+    q = w.q()
+    q[rows] *= 32.0
+    ca.q.copy_(torch.from_numpy(q).to(torch.bfloat16))
+    note("[gpu] second pass: mixed rows")
+    b = ca.forward()
+    torch.cuda.synchronize()
+    keep = torch.ones(w.nq, dtype=torch.bool, device="cuda")
+    keep[rows] = False
+    assert torch.equal(a[keep], b[keep])
+    from oracle import attn64
+    segs = [(*w.kv(i), s.pos) for i, s in enumerate(w.segments)]
+    ref = attn64.chunk_attention(q, None, segs, w.axis_dims, w.theta, w.scale, rows=np.array(rows))
+    got = b[rows].float().cpu().numpy().astype(np.float64)
+    rel, mx = assert_parity(got, ref, "bf16", "scaled rows")
+    note(f"  scaled rows rel-L2 {rel:.3e} max-abs {mx:.3e}")
