@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="full_1344x768")
     p.add_argument("--cpu-rows", type=int, default=2560, help="query rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--qk-norm", action="store_true",
+                   help="fuse per-head RMS QK-norm (shared weights) into the pack and the query load")
     p.add_argument("--no-shard", action="store_true",
                    help="skip the extra measurement of one GPU's head shard (40/8 = 5 heads)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -161,6 +163,9 @@ def main():
     from streaming_video_diffusion_amd.stream import ChunkAttention
 
     w = I.CONFIGS[args.workload]()
+    if args.qk_norm:
+        import dataclasses
+        w = dataclasses.replace(w, name=w.name + "_qknorm", qk_norm="shared")
     calls = [ChunkAttention(w, call=c, device="cuda:0") for c in range(w.calls)]
     stream = torch.cuda.current_stream()
     for ca in calls:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 /* Packed context capacity (rows) must be a multiple of this (one key tile). */
 #define SA_ROW_ALIGN 64
@@ -103,6 +103,28 @@ sa_status sa_make_rope_tables(const sa_rope_spec *spec, const float *pos_thw, in
                               hipStream_t stream);
 
 /*
+ * Per-head RMS normalisation of a query or key row (QK-norm), applied to the
+ * row as it is loaded, before its rotation: over the head_dim elements x_c of
+ * one head,  x_c -> x_c / sqrt(mean_c(x_c^2) + eps) * weight[c].
+ * (The MiniMax-H3 DiT normalises queries and keys before its 3D RoPE:
+ * MiniMax-H3 deep-dive page, attention paragraph after the DiT configuration
+ * table; the pages do not give its form, this is the plain RMSNorm reading.)
+ * weight:   device float32 [head_dim] shared by all heads, or
+ *           [heads][head_dim] when per_head != 0; NULL means all ones.
+ *           16-byte aligned.
+ * eps:      finite, >= 0.
+ * per_head: 0 or 1.
+ * The mean square is formed in float32 from the row's elements (exact bf16 or
+ * float32 values), the scale is 1/sqrt in float32, and the normalised row
+ * stays float32 until the single rounding after its rotation.
+ */
+typedef struct {
+    const float *weight;
+    float eps;
+    int32_t per_head;
+} sa_rmsnorm;
+
+/*
  * One source segment of the key/value context (style prompt, reference frame,
  * a history tier, or the current chunk).
  * Element (row r, head h, dim c) of K is at k[r*k_row_stride + h*k_head_stride + c],
@@ -119,6 +141,8 @@ typedef struct {
     const float *rope;     /* device [rows][head_dim/2][2] table from sa_make_rope_tables,
                               or NULL: keys used unrotated (the persistent prompt K/V) */
     int64_t dst_row;       /* first packed row this segment fills */
+    const sa_rmsnorm *k_norm; /* host pointer, or NULL: keys taken as given. When set, every key
+                                 row is RMS-normalised (before its rotation, if any) */
 } sa_segment;
 
 /*
@@ -164,8 +188,9 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
  * sa_pack_context -- gather segments into the packed K/V buffers.
  *
  * Each segment's rows are written to packed rows [dst_row, dst_row + rows),
- * keys rotated by the segment's table (fused into the load: no separate RoPE
- * pass), values copied (bf16: transposed as documented above). A call that
+ * keys RMS-normalised when the segment has a k_norm and rotated by the
+ * segment's table (both fused into the load: no separate pass), values copied
+ * (bf16: transposed as documented above). A call that
  * packs at least one row also writes zeros to the padding rows [ctx->rows,
  * next multiple of SA_ROW_ALIGN) of every head. Other packed rows not covered
  * by a segment of this call are left untouched, so the static prefix (prompt,
@@ -186,12 +211,15 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
  * q_rope: device [nq][head_dim/2][2] table, or NULL for unrotated queries.
  *         The rotation is fused into the query load (float32 math, one
  *         rounding to bfloat16 on the SA_BF16 path).
+ * q_norm: host pointer, or NULL. When set, every query row is RMS-normalised
+ *         in the same load, before its rotation (QK-norm).
  * softmax_scale: multiplies <q, k> before the softmax (usually 1/sqrt(d)).
  * out:    device [nq][heads][head_dim] of out_dtype (SA_BF16 or SA_F32),
  *         element (r, h, c) at out[r*o_row_stride + h*o_head_stride + c].
  *
- * out[r][h] = sum_j softmax_j(softmax_scale * <R(pq_r) q_rh, K'_jh>) V_jh over
- * all packed rows j < ctx->rows, with no mask (the moving part of the window
+ * out[r][h] = sum_j softmax_j(softmax_scale * <R(pq_r) N(q_rh), K'_jh>) V_jh over
+ * all packed rows j < ctx->rows (N = the q_norm normalisation, or identity),
+ * with no mask (the moving part of the window
  * attends to the whole window: StreamRender-H3 page, streaming-context
  * section). SA_BF16: bf16 matrix-core products with float32 accumulation and
  * float32 online softmax; SA_F32: float32 throughout.
@@ -200,8 +228,9 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
  * [1, capacity]), SA_ERR_DTYPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_HIP.
  */
 sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
-                     int64_t q_head_stride, const float *q_rope, float softmax_scale, void *out,
-                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream);
+                     int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                     void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride,
+                     hipStream_t stream);
 
 /* Static, human-readable name of a status code. Never NULL. */
 const char *sa_status_string(sa_status status);

@@ -10,6 +10,8 @@ What it computes is the plain definition of the operation, in float64:
 
 * ``rope64``  -- 3D (time, height, width) rotary position encoding: angles from
   positions and the per-pair rotation.
+* ``norm64``  -- per-head RMS normalisation of queries and keys (QK-norm),
+  applied before the rotation.
 * ``attn64``  -- dense softmax attention of the current chunk's queries over the
   concatenated key/value context (prompt KV | reference frame | history tiers |
   current chunk), vectorised with numpy per head and query block.
@@ -29,6 +31,6 @@ invariants, a library routine (SDPA) and brute force; nothing is "parity
 unpinned".
 """
 
-from . import rope64, attn64, brute  # noqa: F401
+from . import rope64, norm64, attn64, brute  # noqa: F401
 
-__all__ = ["rope64", "attn64", "brute"]
+__all__ = ["rope64", "norm64", "attn64", "brute"]

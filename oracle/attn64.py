@@ -6,9 +6,10 @@ The operation (plain definition; flash-style online softmax is an exact
 reformulation of it, so this is what a fast kernel must reproduce up to
 rounding):
 
-1. Rotate the queries by their own 3D positions; rotate every key of a
-   rotary segment by that key's positions; keys of a non-rotary segment (the
-   persistent style-prompt key/values) are used as they are.
+1. Optionally RMS-normalise queries and keys per head (QK-norm, see
+   ``norm64``), then rotate the queries by their own 3D positions and every
+   key of a rotary segment by that key's positions; keys of a non-rotary
+   segment (the persistent style-prompt key/values) are not rotated.
    (MiniMax-H3 deep-dive page: dense softmax attention with 3D MM-RoPE.
    AlayaRenderer-Flash page, key contributions / method: prompt-derived
    persistent key/values are added to every self-attention layer.)
@@ -25,7 +26,7 @@ rounding):
 
 import numpy as np
 
-from . import rope64
+from . import norm64, rope64
 
 
 def softmax_rows(s):
@@ -58,29 +59,43 @@ def attention(q, k, v, scale, block=512):
     return out
 
 
-def rotated_keys(segments, axis_dims, theta):
-    """Concatenate segments into (K', V) with each rotary key rotated.
+def prepare(x, pos, norm, axis_dims, theta):
+    """One query or key block ``[n][H][d]`` as attention sees it: QK-norm
+    (``norm`` = ``(weight, eps)`` or ``None``) first, then the rotation by
+    ``pos`` (``[n][3]`` or ``None`` for no rotation)."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[0] == 0:
+        return x
+    if norm is not None:
+        x = norm64.rmsnorm(x, norm[0], norm[1])
+    if pos is not None:
+        x = rope64.rotate(x, rope64.angles(pos, axis_dims, theta))
+    return x
+
+
+def rotated_keys(segments, axis_dims, theta, k_norm=None):
+    """Concatenate segments into (K', V) with each key normalised (when
+    ``k_norm`` is given) and each rotary key rotated.
 
     ``segments``: sequence of ``(k, v, pos)``; ``k``, ``v`` are ``[n][H][d]``
     and ``pos`` is ``[n][3]`` or ``None`` for a non-rotary segment.
     """
     ks, vs = [], []
     for k, v, pos in segments:
-        k = np.asarray(k, dtype=np.float64)
-        if pos is not None and k.shape[0] > 0:
-            k = rope64.rotate(k, rope64.angles(pos, axis_dims, theta))
-        ks.append(k)
+        ks.append(prepare(k, pos, k_norm, axis_dims, theta))
         vs.append(np.asarray(v, dtype=np.float64))
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
 
-def chunk_attention(q, q_pos, segments, axis_dims, theta, scale, rows=None, block=512):
+def chunk_attention(q, q_pos, segments, axis_dims, theta, scale, rows=None, block=512, q_norm=None,
+                    k_norm=None):
     """Attention of the chunk's queries over the segmented context.
 
     ``q``: ``[Nq][H][d]``; ``q_pos``: ``[Nq][3]`` or ``None`` (no rotary);
     ``segments`` as in :func:`rotated_keys`. ``rows`` optionally selects query
     rows (rows are independent, so this is exact for the selected rows).
-    Returns float64 ``[len(rows) or Nq][H][d]``.
+    ``q_norm`` / ``k_norm``: ``(weight, eps)`` QK-norm of queries / of every
+    key, or ``None``. Returns float64 ``[len(rows) or Nq][H][d]``.
     """
     q = np.asarray(q, dtype=np.float64)
     head_dim = q.shape[-1]
@@ -90,9 +105,8 @@ def chunk_attention(q, q_pos, segments, axis_dims, theta, scale, rows=None, bloc
         q = q[rows]
         if q_pos is not None:
             q_pos = np.asarray(q_pos)[rows]
-    if q_pos is not None:
-        q = rope64.rotate(q, rope64.angles(q_pos, axis_dims, theta))
-    k, v = rotated_keys(segments, axis_dims, theta)
+    q = prepare(q, q_pos, q_norm, axis_dims, theta)
+    k, v = rotated_keys(segments, axis_dims, theta, k_norm=k_norm)
     if k.shape[0] == 0:
         raise ValueError("the key/value context is empty")
     return attention(q, k, v, scale, block=block)

@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY. Pure Python loops and ``math.fsum``; no numpy
 arithmetic, so it shares no vectorised code with ``attn64``. It states the same
-definition (3D rotary encoding of queries and rotary keys, then softmax
+definition (optional QK-norm, 3D rotary encoding of queries and rotary keys, then softmax
 attention over all keys with no mask -- MiniMax-H3 deep-dive page, attention
 paragraph after the DiT configuration table; StreamRender-H3 page,
 streaming-context section) one number at a time.
@@ -35,11 +35,28 @@ def rotate_vec(x, p_thw, axis_dims, theta):
     return out
 
 
-def chunk_attention(q, q_pos, segments, axis_dims, theta, scale):
+def rms_vec(x, h, norm):
+    """RMS-normalise one head vector ``x`` of head ``h`` (QK-norm before the
+    rotation): divide by sqrt(mean of squares + eps), multiply by the weight
+    (``norm`` = ``(weight, eps)``; weight ``None``, ``[d]`` or ``[H][d]``)."""
+    weight, eps = norm
+    d = len(x)
+    r = math.sqrt(math.fsum(float(t) * float(t) for t in x) / d + float(eps))
+    if weight is None:
+        w = [1.0] * d
+    elif hasattr(weight[0], "__len__"):
+        w = [float(t) for t in weight[h]]
+    else:
+        w = [float(t) for t in weight]
+    return [float(x[c]) / r * w[c] for c in range(d)]
+
+
+def chunk_attention(q, q_pos, segments, axis_dims, theta, scale, q_norm=None, k_norm=None):
     """Same contract as ``attn64.chunk_attention`` (no row selection).
 
     ``q``: nested ``[Nq][H][d]``; ``q_pos``: ``[Nq][3]`` or ``None``;
-    ``segments``: ``(k, v, pos_or_None)``. Returns nested lists of floats.
+    ``segments``: ``(k, v, pos_or_None)``; ``q_norm`` / ``k_norm``:
+    ``(weight, eps)`` or ``None``. Returns nested lists of floats.
     """
     keys, vals = [], []
     for k, v, pos in segments:
@@ -47,6 +64,8 @@ def chunk_attention(q, q_pos, segments, axis_dims, theta, scale):
             heads_k = []
             for h in range(len(k[j])):
                 kv = [float(t) for t in k[j][h]]
+                if k_norm is not None:
+                    kv = rms_vec(kv, h, k_norm)
                 if pos is not None:
                     kv = rotate_vec(kv, pos[j], axis_dims, theta)
                 heads_k.append(kv)
@@ -57,6 +76,8 @@ def chunk_attention(q, q_pos, segments, axis_dims, theta, scale):
         row = []
         for h in range(len(q[n])):
             qv = [float(t) for t in q[n][h]]
+            if q_norm is not None:
+                qv = rms_vec(qv, h, q_norm)
             if q_pos is not None:
                 qv = rotate_vec(qv, q_pos[n], axis_dims, theta)
             s = [scale * math.fsum(a * b for a, b in zip(qv, keys[j][h])) for j in range(len(keys))]

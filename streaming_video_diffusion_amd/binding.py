@@ -37,11 +37,31 @@ class RopeSpec(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("axis_dims", ctypes.c_int32 * 3), ("theta", ctypes.c_double)]
 
 
+class RmsNorm(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("eps", ctypes.c_float), ("per_head", ctypes.c_int32)]
+
+
 class Segment(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("k_row_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
                 ("v_row_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
-                ("rope", ctypes.c_void_p), ("dst_row", ctypes.c_int64)]
+                ("rope", ctypes.c_void_p), ("dst_row", ctypes.c_int64), ("k_norm", ctypes.c_void_p)]
+
+
+class Norm:
+    """QK-norm spec: ``weight`` float32 [head_dim] (shared by all heads) or
+    [heads][head_dim] (per head) on the device, or None for all ones; ``eps``."""
+
+    def __init__(self, weight=None, eps=1e-6):
+        if weight is not None and (weight.dtype != torch.float32 or weight.dim() not in (1, 2)
+                                   or not weight.is_contiguous()):
+            raise ValueError("norm weight must be a contiguous float32 [head_dim] or [heads][head_dim] tensor")
+        self.weight = weight
+        self.eps = float(eps)
+
+    def struct(self):
+        w = self.weight
+        return RmsNorm(None if w is None else w.data_ptr(), self.eps, 0 if w is None or w.dim() == 1 else 1)
 
 
 class Context(ctypes.Structure):
@@ -68,8 +88,8 @@ def lib():
         L.sa_packed_bytes.restype = i32
         L.sa_pack_context.argtypes = [ctypes.POINTER(Context), ctypes.POINTER(Segment), i32, vp]
         L.sa_pack_context.restype = i32
-        L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.c_float, vp, i32,
-                                 i64, i64, vp]
+        L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                 ctypes.c_float, vp, i32, i64, i64, vp]
         L.sa_forward.restype = i32
         L.sa_status_string.argtypes = [i32]
         L.sa_status_string.restype = ctypes.c_char_p
@@ -156,26 +176,40 @@ class PackedContext:
                        self.k_packed.data_ptr(), self.v_packed.data_ptr())
 
 
-def make_segment(k, v, dst_row, rope=None):
-    """C segment descriptor for K/V views [rows][heads][head_dim] starting at packed row dst_row."""
+def make_segment(k, v, dst_row, rope=None, k_norm=None):
+    """C segment descriptor for K/V views [rows][heads][head_dim] starting at
+    packed row dst_row. ``k_norm`` is a ctypes RmsNorm the caller keeps alive
+    for the call, or None."""
     krs, khs = _rows_heads(k, "k")
     vrs, vhs = _rows_heads(v, "v")
     if k.shape[0] != v.shape[0]:
         raise ValueError("k and v must have the same number of rows")
     return Segment(k.data_ptr(), v.data_ptr(), k.shape[0], krs, khs, vrs, vhs,
-                   None if rope is None else rope.data_ptr(), dst_row)
+                   None if rope is None else rope.data_ptr(), dst_row,
+                   None if k_norm is None else ctypes.cast(ctypes.pointer(k_norm), ctypes.c_void_p))
 
 
-def sa_pack_context(ctx, segments, stream=None):
-    """Pack ``segments`` (list of (k, v, dst_row, rope_or_None)) into ``ctx``."""
-    segs = [make_segment(k, v, dst, rope) for k, v, dst, rope in segments]
+def sa_pack_context(ctx, segments, stream=None, k_norm=None):
+    """Pack ``segments`` (list of (k, v, dst_row, rope_or_None[, norm_or_None]))
+    into ``ctx``. A segment's own norm (a ``Norm``) wins over ``k_norm``, the
+    default for every segment."""
+    keep = []
+    segs = []
+    for seg in segments:
+        k, v, dst, rope = seg[:4]
+        norm = seg[4] if len(seg) > 4 else k_norm
+        n = None if norm is None else norm.struct()
+        keep.append(n)
+        segs.append(make_segment(k, v, dst, rope, n))
     arr = (Segment * max(1, len(segs)))(*segs)
     c = ctx.struct()
     _check("sa_pack_context", lib().sa_pack_context(ctypes.byref(c), arr, len(segs), _stream(stream)))
+    del keep
 
 
-def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None):
-    """Attention of ``q`` [Nq][heads][head_dim] over the packed context."""
+def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None, q_norm=None):
+    """Attention of ``q`` [Nq][heads][head_dim] over the packed context;
+    ``q_norm`` (a ``Norm``) normalises every query row before its rotation."""
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:
         softmax_scale = ctx.head_dim ** -0.5
@@ -183,7 +217,8 @@ def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     ors, ohs = _rows_heads(out, "out")
     c = ctx.struct()
+    qn = None if q_norm is None else q_norm.struct()
     _check("sa_forward", lib().sa_forward(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs, _ptr(q_rope),
-                                          float(softmax_scale), _ptr(out), _DTYPES[out.dtype], ors, ohs,
-                                          _stream(stream)))
+                                          None if qn is None else ctypes.byref(qn), float(softmax_scale),
+                                          _ptr(out), _DTYPES[out.dtype], ors, ohs, _stream(stream)))
     return out

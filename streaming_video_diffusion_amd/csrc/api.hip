@@ -122,6 +122,20 @@ sa_status sa_make_rope_tables(const sa_rope_spec *spec, const float *pos_thw, in
     return SA_OK;
 }
 
+// Validate an optional RMS-norm spec and copy it into the kernel-side form.
+static sa_status check_norm(const sa_rmsnorm *n, const char *what, sa::NormArgs &out) {
+    out = sa::NormArgs{};
+    if (!n) return SA_OK;
+    if (!std::isfinite(n->eps) || n->eps < 0.0f) return fail(SA_ERR_SHAPE, "%s: eps must be finite and >= 0", what);
+    if (n->per_head != 0 && n->per_head != 1) return fail(SA_ERR_SHAPE, "%s: per_head must be 0 or 1", what);
+    if (n->weight && !aligned(n->weight, 16)) return fail(SA_ERR_ALIGN, "%s: weight must be 16-byte aligned", what);
+    out.on = 1;
+    out.weight = n->weight;
+    out.eps = n->eps;
+    out.per_head = n->per_head;
+    return SA_OK;
+}
+
 sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64_t capacity_rows,
                           size_t *bytes_each) {
     g_err[0] = 0;
@@ -177,7 +191,13 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
             if (o.rows > 0 && s.dst_row < o.dst_row + o.rows && o.dst_row < s.dst_row + s.rows)
                 return fail(SA_ERR_SHAPE, "segments %d and %d overlap in the packed rows", j, i);
         }
+        sa::NormArgs kn;
+        char what[32];
+        snprintf(what, sizeof what, "segment %d: k_norm", i);
+        st = check_norm(s.k_norm, what, kn);
+        if (st != SA_OK) return st;
         sa::PackSeg &p = a.seg[used++];
+        p.norm = kn;
         p.k = s.k;
         p.v = s.v;
         p.rope = s.rope;
@@ -202,8 +222,8 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
 }
 
 sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
-                     const float *q_rope, float softmax_scale, void *out, sa_dtype out_dtype, int64_t o_row_stride,
-                     int64_t o_head_stride, hipStream_t stream) {
+                     const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
+                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream) {
     g_err[0] = 0;
     sa_status st = check_context(ctx);
     if (st != SA_OK) return st;
@@ -225,6 +245,8 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
         return fail(SA_ERR_SHAPE, "a q / out stride is smaller than head_dim");
 
     sa::FwdArgs a{};
+    st = check_norm(q_norm, "q_norm", a.q_norm);
+    if (st != SA_OK) return st;
     a.q = q;
     a.q_rope = q_rope;
     a.k = ctx->k_packed;

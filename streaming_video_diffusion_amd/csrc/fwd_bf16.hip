@@ -9,8 +9,9 @@
 //
 // Work decomposition: a workgroup of NW waves owns NW*32 query rows of one
 // head; each wave owns 32 queries, two waves share a SIMD.
-//   * Q is rotated in fp32, multiplied by scale*log2(e), rounded once to
-//     bf16 and kept in registers as the B operand of v_mfma_f32_32x32x16_bf16;
+//   * Q is RMS-normalised when asked (QK-norm) and rotated in fp32,
+//     multiplied by scale*log2(e), rounded once to bf16 and kept in registers
+//     as the B operand of v_mfma_f32_32x32x16_bf16;
 //   * scores are formed transposed, S^T = K Q^T (A = K tile from LDS), so the
 //     32x32 accumulator puts one query column in each lane: a row max is an
 //     in-lane reduction plus one exchange between half-waves, and the row sum
@@ -184,15 +185,36 @@ void fwd_bf16_kernel(FwdArgs a) {
         const bool valid = q_row < a.nq;
         const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + q_row * a.q_rs + (int64_t)head * a.q_hs;
         const float *tb = a.q_rope ? a.q_rope + q_row * D : nullptr;  // [row][D/2][2]
+        bf16x8 qraw[DC];
+#pragma unroll
+        for (int j = 0; j < DC; ++j) qraw[j] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * j + 8 * hf) : bf16x8{};
+        // QK-norm: the row's mean square over both half-waves' elements, in
+        // float32, before the rotation.
+        float qs = 1.0f;
+        const float *qw = nullptr;
+        if (a.q_norm.on) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < DC; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = __builtin_fmaf((float)qraw[j][e], (float)qraw[j][e], ss);
+            ss += half_swap_partner(ss);
+            qs = valid ? 1.0f / __builtin_sqrtf(ss / (float)D + a.q_norm.eps) : 0.0f;
+            if (a.q_norm.weight) qw = a.q_norm.weight + (a.q_norm.per_head ? (int64_t)head * D : 0);
+        }
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
             const int dcol = 16 * j + 8 * hf;
             bf16x8 x = bf16x8{};
             if (valid) {
-                const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(qp + dcol);
+                const bf16x8 raw = qraw[j];
                 float xf[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xf[e] = (float)raw[e];
+                if (a.q_norm.on) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xf[e] = xf[e] * qs * (qw ? qw[dcol + e] : 1.0f);
+                }
                 if (tb) {
                     const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tb + dcol);
                     const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tb + dcol + 4);

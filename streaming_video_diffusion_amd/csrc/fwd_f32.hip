@@ -4,7 +4,8 @@
 // queries over every packed (already rotated) key, no mask (MiniMax-H3
 // deep-dive page, attention paragraph after the DiT configuration table;
 // StreamRender-H3 page, streaming-context section) -- in float32 end to end:
-// float32 rotation, float32 dot products, accurate expf, float32 sums. Two
+// float32 RMS normalisation (when asked) and rotation, float32 dot products,
+// accurate expf, float32 sums. Two
 // lanes share one query (each holds half of the head dimension), 64 queries
 // per workgroup; K/V tiles of 32 keys are staged in LDS and read by
 // broadcast. This path is for small f32 problems and is not tuned.
@@ -36,12 +37,29 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     {
         const float *qp = reinterpret_cast<const float *>(a.q) + row * a.q_rs + (int64_t)head * a.q_hs + half * H2;
         const float *tb = a.q_rope ? a.q_rope + row * D + half * H2 : nullptr;
+        // QK-norm: mean square of the row over both lanes' halves, before the rotation.
+        float qs = 1.0f;
+        const float *qw = nullptr;
+        if (a.q_norm.on) {
+            float ss = 0.f;
+            if (valid) {
+#pragma unroll
+                for (int e = 0; e < H2; ++e) ss = __builtin_fmaf(qp[e], qp[e], ss);
+            }
+            ss += __shfl_xor(ss, 1);
+            qs = valid ? 1.0f / __builtin_sqrtf(ss / (float)D + a.q_norm.eps) : 0.0f;
+            if (a.q_norm.weight) qw = a.q_norm.weight + (a.q_norm.per_head ? (int64_t)head * D : 0) + half * H2;
+        }
 #pragma unroll
         for (int e = 0; e < H2; e += 2) {
             float x0 = 0.f, x1 = 0.f;
             if (valid) {
                 x0 = qp[e];
                 x1 = qp[e + 1];
+                if (a.q_norm.on) {
+                    x0 *= qs * (qw ? qw[e] : 1.0f);
+                    x1 *= qs * (qw ? qw[e + 1] : 1.0f);
+                }
                 if (tb) {
                     const float c = tb[e], s = tb[e + 1];
                     const float r0 = x0 * c - x1 * s;

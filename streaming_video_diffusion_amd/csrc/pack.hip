@@ -5,15 +5,17 @@
 // inference-acceleration section), and fuse rotary encoding with the cache
 // write (same page, Fast Causal H3 VAE section). Here one workgroup owns one
 // 64-row tile of the packed row space for one head and one segment:
-//   * keys: 16-byte coalesced loads, rotation in float32 by the segment's
-//     table, one rounding to bfloat16, 16-byte stores into K [H][C][d];
+//   * keys: 16-byte coalesced loads, optional RMS normalisation (QK-norm) and
+//     rotation in float32 by the segment's table, one rounding to bfloat16,
+//     16-byte stores into K [H][C][d];
 //   * values (bf16): staged through LDS and written transposed into
 //     V [H][d][C] with the 16-row group permutation the forward kernel's
 //     matrix-core operand wants, 128 contiguous bytes per 8 lanes;
 //   * values (f32): copied row-major.
-// Rows outside the segment are never written, so the static prefix survives
-// an in-place rewrite of the dynamic rows. This pass is HBM-bound: each
-// element is read once and written once.
+// Rows outside the segment are never written by this kernel, so the static
+// prefix survives an in-place rewrite of the dynamic rows; the padding rows
+// after the last valid row are zeroed by zero_pad_kernel below. This pass is
+// HBM-bound: each element is read once and written once.
 #include "sa_internal.h"
 
 namespace sa {
@@ -25,6 +27,24 @@ constexpr int kThreads = 256;
 // Stored column j (within a 16-row group) holds packed row perm(j) of the
 // group; perm swaps 4..7 with 8..11 and is its own inverse.
 __device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+// RMS normalisation of one key row held by CH consecutive lanes, E elements
+// per lane starting at element c0 of the row (QK-norm, applied before the
+// rotation): the row's mean square is summed across those lanes in float32.
+// Every lane of a CH-lane group is active or inactive together (one row per
+// group), so the exchange stays within active lanes.
+template <int CH, int E>
+__device__ __forceinline__ void norm_row(float (&x)[E], const NormArgs &n, int h, int d, int c0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int m = 1; m < CH; m <<= 1) ss += __shfl_xor(ss, m);
+    const float r = 1.0f / __builtin_sqrtf(ss / (float)d + n.eps);
+    const float *w = n.weight ? n.weight + (n.per_head ? (int64_t)h * d : 0) + c0 : nullptr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = x[e] * r * (w ? w[e] : 1.0f);
+}
 
 struct TileRange {
     int64_t tile_start, lo, hi;  // packed rows [lo, hi) of this tile belong to the segment
@@ -67,22 +87,26 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
         const int64_t row = r.tile_start + lr;
         if (row < r.lo || row >= r.hi) continue;
         const int64_t sr = row - s.dst_row;
-        bf16x8 kv = *reinterpret_cast<const bf16x8 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 8);
+        const bf16x8 kraw = *reinterpret_cast<const bf16x8 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 8);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)kraw[e];
+        if (s.norm.on) norm_row<CH, 8>(x, s.norm, h, D, chunk * 8);
         if (s.rope) {
             const f32x4 *tb = reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 4) * 2);
             const f32x4 t0 = tb[0], t1 = tb[1];
             const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)kv[e];
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
                 const float c = cs[2 * pr], sn = cs[2 * pr + 1];
                 const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
-                kv[2 * pr] = (bf16)(x0 * c - x1 * sn);
-                kv[2 * pr + 1] = (bf16)(x0 * sn + x1 * c);
+                x[2 * pr] = x0 * c - x1 * sn;
+                x[2 * pr + 1] = x0 * sn + x1 * c;
             }
         }
+        bf16x8 kv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = (bf16)x[e];
         *reinterpret_cast<bf16x8 *>(kp + row * D + chunk * 8) = kv;
         const bf16x8 vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
         *reinterpret_cast<bf16x8 *>(sv + lr * PITCH + chunk * 8) = vv;
@@ -142,6 +166,11 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
         if (row < r.lo || row >= r.hi) continue;
         const int64_t sr = row - s.dst_row;
         f32x4 kv = *reinterpret_cast<const f32x4 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 4);
+        if (s.norm.on) {
+            float x[4] = {kv.x, kv.y, kv.z, kv.w};
+            norm_row<CH, 4>(x, s.norm, h, D, chunk * 4);
+            kv = f32x4{x[0], x[1], x[2], x[3]};
+        }
         if (s.rope) {
             const f32x4 cs = *reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 2) * 2);
             const f32x4 x = kv;

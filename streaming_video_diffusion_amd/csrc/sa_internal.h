@@ -31,12 +31,21 @@ struct RopeTableArgs {
 };
 hipError_t launch_rope_tables(const RopeTableArgs &a, hipStream_t stream);
 
+// --- QK-norm ----------------------------------------------------------------
+struct NormArgs {
+    const float *weight;  // [head_dim] or [heads][head_dim]; NULL = ones
+    float eps;
+    int32_t per_head;
+    int32_t on;
+};
+
 // --- context pack ---------------------------------------------------------
 struct PackSeg {
     const void *k;
     const void *v;
     const float *rope;
     int64_t rows, k_rs, k_hs, v_rs, v_hs, dst_row;
+    NormArgs norm;
 };
 struct PackArgs {
     void *k_packed;
@@ -64,6 +73,7 @@ struct FwdArgs {
     int32_t out_f32;
     float scale;       // softmax scale
     float scale_log2;  // softmax scale * log2(e)
+    NormArgs q_norm;
 };
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream);
 int fwd_bf16_rows_per_workgroup();  // query rows one bf16 forward workgroup owns

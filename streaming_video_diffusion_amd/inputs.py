@@ -112,6 +112,8 @@ class Workload:
     description: str = ""
     q_rows: int = None          # Nq; taken from q_pos when that is given
     meta: dict = field(default_factory=dict)
+    qk_norm: str = None         # None, "shared" ([d] weights) or "per_head" ([H][d] weights)
+    norm_eps: float = 1e-6
 
     def __post_init__(self):
         if self.q_rows is None:
@@ -147,6 +149,18 @@ class Workload:
         """Keys and values of segment index ``seg`` for call ``call``."""
         rows = self.segments[seg].rows
         return self._draw(call, 1 + 2 * seg, rows), self._draw(call, 2 + 2 * seg, rows)
+
+    def norm_weights(self):
+        """QK-norm weights (query, key): float32 [d] or [H][d], drawn as
+        1 + 0.2 N(0, 1); ``None`` when the workload has no QK-norm."""
+        if self.qk_norm is None:
+            return None
+        shape = (self.head_dim,) if self.qk_norm == "shared" else (self.heads, self.head_dim)
+        out = []
+        for tensor_id in (900, 901):
+            rng = np.random.default_rng(np.random.SeedSequence([ENTROPY, self.cfg_id, tensor_id]))
+            out.append((1.0 + 0.2 * rng.standard_normal(shape)).astype(np.float32))
+        return tuple(out)
 
 
 def _video_segments(prompt, grid_h, grid_w, ref_t, tiers, cur_t, audio=0):
@@ -207,7 +221,7 @@ CONFIGS = {w().name: w for w in (tiny_f32, lowres_bf16, full_1344x768, hier_1344
 
 
 def custom(name, cfg_id, dtype, heads, head_dim, seg_rows, nq, rotary=True, prompt_rows=0,
-           pos_scale=40.0, axis_dims=None, theta=ROPE_THETA, scale=None):
+           pos_scale=40.0, axis_dims=None, theta=ROPE_THETA, scale=None, qk_norm=None):
     """Arbitrary-shape workload for tests: random positions, given row counts.
 
     ``seg_rows``: rows of each rotary segment after an optional prompt
@@ -225,4 +239,4 @@ def custom(name, cfg_id, dtype, heads, head_dim, seg_rows, nq, rotary=True, prom
     for i, r in enumerate(seg_rows):
         segs.append(Segment(f"seg{i}", int(r), pos(int(r)), True))
     return Workload(name, cfg_id, dtype, heads, head_dim, pos(nq) if rotary else None, segs,
-                    axis_dims=axis_dims, theta=theta, scale=scale, q_rows=nq)
+                    axis_dims=axis_dims, theta=theta, scale=scale, q_rows=nq, qk_norm=qk_norm)

@@ -57,6 +57,11 @@ class ChunkAttention:
             self.segs.append(dict(name=s.name, k=up(k), v=up(v), pos=pos, table=table, dst=row,
                                   dynamic=s.dynamic, rotary=s.pos is not None, shares_q=shares_q))
             row += s.rows
+        self.q_norm = self.k_norm = None
+        weights = w.norm_weights()
+        if weights is not None:
+            qw, kw = (torch.from_numpy(x).to(dev) for x in weights)
+            self.q_norm, self.k_norm = B.Norm(qw, w.norm_eps), B.Norm(kw, w.norm_eps)
         self.ctx = B.PackedContext(w.heads, w.head_dim, self.dtype, w.nk, device=dev)
         self.ctx.rows = w.nk
         self.out = torch.empty((w.nq, w.heads, w.head_dim), dtype=self.out_dtype, device=dev)
@@ -76,7 +81,7 @@ class ChunkAttention:
                 continue
             rope = self.q_table if s["shares_q"] else (s["table"] if s["rotary"] else None)
             segs.append((s["k"], s["v"], s["dst"], rope))
-        B.sa_pack_context(self.ctx, segs, stream=stream)
+        B.sa_pack_context(self.ctx, segs, stream=stream, k_norm=self.k_norm)
 
     def pack_static(self, stream=None):
         """Build the static prefix's tables and pack it (once per bank)."""
@@ -91,7 +96,7 @@ class ChunkAttention:
         return self.forward(stream)
 
     def forward(self, stream=None):
-        B.sa_forward(self.ctx, self.q, self.q_table, self.w.scale, out=self.out, stream=stream)
+        B.sa_forward(self.ctx, self.q, self.q_table, self.w.scale, out=self.out, stream=stream, q_norm=self.q_norm)
         return self.out
 
     def host_inputs(self):
@@ -102,3 +107,10 @@ class ChunkAttention:
             k, v = w.kv(i, self.call)
             segs.append((k, v, s.pos))
         return w.q(self.call), w.q_pos, segs
+
+    def host_norms(self):
+        """QK-norm of queries and keys as ``(weight, eps)`` host pairs, or ``(None, None)``."""
+        weights = self.w.norm_weights()
+        if weights is None:
+            return None, None
+        return (weights[0], self.w.norm_eps), (weights[1], self.w.norm_eps)

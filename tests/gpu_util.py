@@ -66,5 +66,6 @@ def run(workload, call=0, out_dtype=None):
 
 def oracle(ca, rows=None):
     q, q_pos, segs = ca.host_inputs()
+    qn, kn = ca.host_norms()
     w = ca.w
-    return attn64.chunk_attention(q, q_pos, segs, w.axis_dims, w.theta, w.scale, rows=rows)
+    return attn64.chunk_attention(q, q_pos, segs, w.axis_dims, w.theta, w.scale, rows=rows, q_norm=qn, k_norm=kn)

@@ -7,9 +7,10 @@ twin ``oracle.brute``. ``test_oracle_pins.py`` runs them on the real oracle;
 ``test_oracle_mutations.py`` plants plausible mistakes in the oracle (on the
 CPU) and checks that some pin fails for each.
 
-The definition pinned: 3D rotary encoding over (t, h, w) bands of the head
-dimension, adjacent rotary pairs, angle ``p_a * theta**(-2i/D_a)``,
-counter-clockwise turn; dense softmax attention over every key with no mask
+The definition pinned: optional per-head RMS normalisation (QK-norm) before
+the rotation; 3D rotary encoding over (t, h, w) bands of the head dimension,
+adjacent rotary pairs, angle ``p_a * theta**(-2i/D_a)``, counter-clockwise
+turn; dense softmax attention over every key with no mask
 (MiniMax-H3 deep-dive page, attention paragraph after the DiT configuration
 table; StreamRender-H3 page, streaming-context section).
 """
@@ -19,7 +20,7 @@ import math
 import numpy as np
 import torch
 
-from oracle import attn64, brute, rope64
+from oracle import attn64, brute, norm64, rope64
 
 AX128 = (32, 48, 48)
 THETA = 10000.0
@@ -252,6 +253,75 @@ def pin_row_selection():
     _close(part, full[rows], 1e-14, "row selection")
 
 
+def pin_rmsnorm_closed_form():
+    """A constant row c*(1..1) normalises to c / sqrt(c^2 + eps) * w, exactly."""
+    rng = _rng(101)
+    for d, c, eps in [(4, 3.0, 0.0), (8, -0.25, 1e-2), (128, 7.5, 1e-6), (64, 1e-3, 1e-6)]:
+        w = rng.standard_normal(d)
+        x = np.full((1, 1, d), c)
+        got = norm64.rmsnorm(x, w, eps)[0, 0]
+        _close(got, c / math.sqrt(c * c + eps) * w, 1e-14, f"rmsnorm closed form d={d}")
+
+
+def pin_rmsnorm_invariants():
+    """eps = 0: scale-invariant, odd, unit mean square; the weight multiplies element-wise."""
+    rng = _rng(102)
+    x = rng.standard_normal((5, 3, 128))
+    w = rng.standard_normal((3, 128))
+    y = norm64.rmsnorm(x, None, 0.0)
+    _close(norm64.rmsnorm(37.5 * x, None, 0.0), y, 1e-13, "rmsnorm scale invariance")
+    _close(norm64.rmsnorm(-x, None, 0.0), -y, 1e-15, "rmsnorm odd")
+    _close(np.mean(y * y, axis=-1), np.ones((5, 3)), 1e-13, "rmsnorm unit mean square")
+    _close(norm64.rmsnorm(x, w, 0.0), y * w, 1e-15, "rmsnorm per-head weight")
+    _close(norm64.rmsnorm(x, w[1], 1e-3), norm64.rmsnorm(x, None, 1e-3) * w[1], 1e-15, "rmsnorm shared weight")
+
+
+def pin_brute_force_qknorm():
+    """With QK-norm (shared and per-head weights), vectorised oracle == scalar twin."""
+    cases = [(111, 8, (2, 2, 4), 2, [4, 2], 3, 2, False), (112, 128, AX128, 2, [3, 2], 2, 1, True),
+             (113, 64, (16, 24, 24), 1, [5], 2, 0, False)]
+    for tag, d, ax, heads, rows, nq, prompt, per_head in cases:
+        q, qp, segs = _tiny_case(tag, d, ax, heads, rows, nq, prompt)
+        rng = _rng(tag + 1000)
+        shape = (heads, d) if per_head else (d,)
+        qn = (1.0 + 0.3 * rng.standard_normal(shape), 1e-3)
+        kn = (1.0 + 0.3 * rng.standard_normal(shape), 1e-5)
+        scale = 1.0 / math.sqrt(d)
+        got = attn64.chunk_attention(3.0 * q, qp, segs, ax, THETA, scale, q_norm=qn, k_norm=kn)
+        ref = brute.chunk_attention((3.0 * q).tolist(), qp.tolist(),
+                                    [(k.tolist(), v.tolist(), None if p is None else p.tolist()) for k, v, p in segs],
+                                    ax, THETA, scale, q_norm=(qn[0].tolist(), qn[1]), k_norm=(kn[0].tolist(), kn[1]))
+        _close(got, ref, 1e-12, f"brute force with QK-norm d={d}")
+
+
+def pin_qknorm_then_rotation():
+    """One rotary pair (d = 2), two keys: the score of each key has a closed
+    form when the row is normalised first and rotated after; with a
+    non-uniform weight the other order gives a different result."""
+    w = np.array([1.5, 0.5])
+    eps = 0.0
+    q = np.array([[[0.8, -1.1]]])
+    k = np.array([[[1.3, 0.2]], [[-0.4, 0.9]]])
+    v = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    pq, pk = np.array([[2.0, 0.0, 0.0]]), np.array([[0.5, 0.0, 0.0], [-1.25, 0.0, 0.0]])
+
+    def nrm(x):
+        r = math.sqrt((x[0] ** 2 + x[1] ** 2) / 2 + eps)
+        return (x[0] / r * w[0], x[1] / r * w[1])
+
+    qa, qb = nrm(q[0, 0])
+    s = []
+    for j in range(2):
+        ka, kb_ = nrm(k[j, 0])
+        delta = pk[j, 0] - pq[0, 0]   # angle of the key minus the angle of the query (theta^0 = 1)
+        s.append(qa * (ka * math.cos(delta) - kb_ * math.sin(delta)) + qb * (ka * math.sin(delta) + kb_ * math.cos(delta)))
+    p1 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+    ref = np.array([[[p1, 1.0 - p1]]])
+    got = attn64.chunk_attention(q, pq, [(k, v, pk)], (2, 0, 0), THETA, 1.0, q_norm=(w, eps), k_norm=(w, eps))
+    _close(got, ref, 1e-13, "norm then rotation, one pair")
+
+
 ALL_PINS = [pin_brute_force, pin_rotation_closed_form, pin_rotation_group, pin_single_pair_scores,
             pin_softmax_rows, pin_constant_v, pin_joint_permutation, pin_zero_angle_is_sdpa,
-            pin_two_keys, pin_degenerate, pin_translation, pin_row_selection]
+            pin_two_keys, pin_degenerate, pin_translation, pin_row_selection, pin_rmsnorm_closed_form,
+            pin_rmsnorm_invariants, pin_brute_force_qknorm, pin_qknorm_then_rotation]

@@ -47,12 +47,14 @@ def test_header_constants_match_binding():
     for name, val in ERR.items():
         assert re.search(rf"#define SA_ERR_{name} \({val}\)", text), name
     assert ctypes.sizeof(B.RopeSpec) == 24
-    assert ctypes.sizeof(B.Segment) == 72
+    assert ctypes.sizeof(B.Segment) == 80
     assert ctypes.sizeof(B.Context) == 48
+    assert ctypes.sizeof(B.RmsNorm) == 16
+    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 2
 
 
 def test_version_and_status_strings(L):
-    assert L.sa_abi_version() == 1
+    assert L.sa_abi_version() == 2
     assert L.sa_status_string(0) == b"SA_OK"
     for name, val in ERR.items():
         assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
@@ -109,12 +111,22 @@ def ctx(**kw):
                      c["v_packed"])
 
 
+_KEEP = []
+
+
+def norm(weight=None, eps=1e-6, per_head=0):
+    n = B.RmsNorm(weight, eps, per_head)
+    _KEEP.append(n)
+    return n
+
+
 def seg(**kw):
     s = dict(k=FAKE, v=FAKE, rows=16, k_row_stride=256, k_head_stride=128, v_row_stride=256, v_head_stride=128,
-             rope=None, dst_row=0)
+             rope=None, dst_row=0, k_norm=None)
     s.update(kw)
+    kn = None if s["k_norm"] is None else ctypes.cast(ctypes.pointer(s["k_norm"]), ctypes.c_void_p)
     return B.Segment(s["k"], s["v"], s["rows"], s["k_row_stride"], s["k_head_stride"], s["v_row_stride"],
-                     s["v_head_stride"], s["rope"], s["dst_row"])
+                     s["v_head_stride"], s["rope"], s["dst_row"], kn)
 
 
 @pytest.mark.parametrize("c,segs,err", [
@@ -136,6 +148,10 @@ def seg(**kw):
     (ctx(), [seg(k_row_stride=260)], "ALIGN"),
     (ctx(), [seg(k_head_stride=64)], "SHAPE"),
     (ctx(), [seg(rope=FAKE + 4)], "ALIGN"),
+    (ctx(), [seg(k_norm=norm(eps=-1.0))], "SHAPE"),
+    (ctx(), [seg(k_norm=norm(eps=float("nan")))], "SHAPE"),
+    (ctx(), [seg(k_norm=norm(per_head=2))], "SHAPE"),
+    (ctx(), [seg(k_norm=norm(weight=FAKE + 4))], "ALIGN"),
 ])
 def test_pack_errors(L, c, segs, err):
     arr = (B.Segment * len(segs))(*segs)
@@ -155,9 +171,9 @@ def test_pack_segment_count_limits(L):
 
 
 def fwd(L, c, q=FAKE, nq=8, qrs=256, qhs=128, rope=None, scale=0.1, out=FAKE * 3, odt=B.SA_BF16, ors=256,
-        ohs=128):
-    return L.sa_forward(None if c is None else ctypes.byref(c), q, nq, qrs, qhs, rope, scale, out, odt, ors, ohs,
-                        None)
+        ohs=128, qn=None):
+    return L.sa_forward(None if c is None else ctypes.byref(c), q, nq, qrs, qhs, rope,
+                        None if qn is None else ctypes.byref(qn), scale, out, odt, ors, ohs, None)
 
 
 def test_forward_errors(L):
@@ -174,6 +190,9 @@ def test_forward_errors(L):
     assert fwd(L, ctx(), odt=B.SA_F32, ors=258) == ERR["ALIGN"]
     assert fwd(L, ctx(), qhs=64) == ERR["SHAPE"]
     assert fwd(L, ctx(head_dim=64), ors=32) == ERR["SHAPE"]
+    assert fwd(L, ctx(), qn=norm(eps=-0.5)) == ERR["SHAPE"]
+    assert fwd(L, ctx(), qn=norm(per_head=-1)) == ERR["SHAPE"]
+    assert fwd(L, ctx(), qn=norm(weight=FAKE + 8)) == ERR["ALIGN"]
     # nq == 0 enqueues nothing and succeeds
     assert fwd(L, ctx(), nq=0) == 0
     assert L.sa_last_error() == b""

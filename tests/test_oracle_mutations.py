@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle_pins
-from oracle import attn64, rope64
+from oracle import attn64, norm64, rope64
 
 
 def _rotate_with(fn):
@@ -74,13 +74,52 @@ def _attention_with(weighted, softmax_axis=-1, use_scale=True):
     return attention
 
 
-def _rotated_keys_unrotated(segments, axis_dims, theta):
+def _rotated_keys_unrotated(segments, axis_dims, theta, k_norm=None):
     ks = [np.asarray(k, dtype=np.float64) for k, _, _ in segments]
     vs = [np.asarray(v, dtype=np.float64) for _, v, _ in segments]
     return np.concatenate(ks), np.concatenate(vs)
 
 
+def _rms_with(denom):
+    def rmsnorm(x, weight, eps):
+        x = np.asarray(x, dtype=np.float64)
+        y = x / denom(x, float(eps))
+        return y if weight is None else y * np.asarray(weight, dtype=np.float64)
+    return rmsnorm
+
+
+def _rms_weight_first(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    if weight is not None:
+        x = x * np.asarray(weight, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _prepare_rotate_first(x, pos, norm, axis_dims, theta):
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[0] == 0:
+        return x
+    if pos is not None:
+        x = rope64.rotate(x, rope64.angles(pos, axis_dims, theta))
+    if norm is not None:
+        x = norm64.rmsnorm(x, norm[0], norm[1])
+    return x
+
+
+def _prepare_norm_ignored(x, pos, norm, axis_dims, theta):
+    x = np.asarray(x, dtype=np.float64)
+    if pos is not None and x.shape[0] > 0:
+        x = rope64.rotate(x, rope64.angles(pos, axis_dims, theta))
+    return x
+
+
 MUTATIONS = {
+    "rms_sum_not_mean": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.sqrt(np.sum(x * x, -1, keepdims=True) + e)))],
+    "rms_no_sqrt": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.mean(x * x, -1, keepdims=True) + e))],
+    "rms_eps_outside_sqrt": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.sqrt(np.mean(x * x, -1, keepdims=True)) + e))],
+    "rms_weight_before_norm": [(norm64, "rmsnorm", _rms_weight_first)],
+    "norm_after_rotation": [(attn64, "prepare", _prepare_rotate_first)],
+    "norm_ignored": [(attn64, "prepare", _prepare_norm_ignored)],
     "clockwise_turn": [(rope64, "rotate", _rotate_with(_adjacent(
         lambda xe, xo, c, s: (xe * c + xo * s, -xe * s + xo * c))))],
     "cos_sin_swapped": [(rope64, "rotate", _rotate_with(_adjacent(
