@@ -57,6 +57,8 @@ extern "C" {
 #define SA_ROW_ALIGN 64
 /* Most segments one sa_pack_context call accepts. */
 #define SA_MAX_SEGMENTS 16
+/* Most key splits of sa_forward_split / sa_combine_splits. */
+#define SA_MAX_SPLITS 256
 
 typedef int32_t sa_status;
 #define SA_OK 0
@@ -231,6 +233,41 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
                      int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
                      void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride,
                      hipStream_t stream);
+
+/*
+ * sa_forward_split -- split-KV form of sa_forward for problems with few query
+ * rows (the 40 audio-only queries of a joint chunk, or one GPU's head shard),
+ * where one workgroup per (query tile, head) cannot fill the chip.
+ *
+ * The packed keys are cut into n_splits runs of whole 64-key tiles, run s
+ * covering tiles [floor(s T / n_splits), floor((s+1) T / n_splits)) of the
+ * T = ceil(ctx->rows / 64) tiles, and each run is processed by its own
+ * workgroups. For every run s, query row r and head h it writes
+ *   partial[s][r][h][0..head_dim) = softmax attention of that row over the
+ *                                   run's keys alone (float32),
+ *   lse[s][r][h]                  = log sum_j exp(softmax_scale * <q', k'_j>)
+ *                                   over the run's keys (natural log, float32).
+ * sa_combine_splits then yields exactly the sa_forward result: softmax over a
+ * union of disjoint key sets is the LSE-weighted mean of the per-set softmax
+ * attentions. Arguments as in sa_forward; partial is device float32
+ * [n_splits][nq][heads][head_dim] (16-byte aligned), lse device float32
+ * [n_splits][nq][heads]; 1 <= n_splits <= min(SA_MAX_SPLITS, T).
+ * Errors: as sa_forward; SA_ERR_SHAPE for n_splits.
+ */
+sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                           int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                           int32_t n_splits, float *partial, float *lse, hipStream_t stream);
+
+/*
+ * sa_combine_splits -- merge sa_forward_split results:
+ *   out[r][h] = sum_s w_s partial[s][r][h] / sum_s w_s,  w_s = exp(lse[s][r][h] - max_s lse[s][r][h]).
+ * out: device [nq][heads][head_dim] of out_dtype with the given element strides.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED (head_dim),
+ * SA_ERR_ALIGN, SA_ERR_HIP.
+ */
+sa_status sa_combine_splits(int32_t n_splits, int64_t nq, int32_t heads, int32_t head_dim, const float *partial,
+                            const float *lse, void *out, sa_dtype out_dtype, int64_t o_row_stride,
+                            int64_t o_head_stride, hipStream_t stream);
 
 /* Static, human-readable name of a status code. Never NULL. */
 const char *sa_status_string(sa_status status);

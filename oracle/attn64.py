@@ -22,6 +22,11 @@ rounding):
    window is bidirectional and its moving part attends to the whole window:
    StreamRender-H3 page, streaming-context section), scaled by ``scale``;
    softmax over keys; weighted sum of the values.
+
+``split_attention`` states the same attention restricted to runs of keys:
+each run's own softmax attention and the natural log of the sum of
+``exp(scores)`` over the run (what a split-key evaluation must produce
+before its runs are merged).
 """
 
 import numpy as np
@@ -110,3 +115,43 @@ def chunk_attention(q, q_pos, segments, axis_dims, theta, scale, rows=None, bloc
     if k.shape[0] == 0:
         raise ValueError("the key/value context is empty")
     return attention(q, k, v, scale, block=block)
+
+
+def split_attention(q, k, v, scale, key_ranges):
+    """Per key run ``[a, b)``: softmax attention over the run's keys alone and
+    ``log sum_j exp(scale * <q, k_j>)`` over the run (natural log).
+
+    ``q``: ``[Nq][H][d]``; ``k``, ``v``: ``[Nk][H][d]``. Returns
+    ``(partial [runs][Nq][H][d], lse [runs][Nq][H])``, float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, heads, d = q.shape
+    partial = np.empty((len(key_ranges), nq, heads, d))
+    lse = np.empty((len(key_ranges), nq, heads))
+    for r, (a, b) in enumerate(key_ranges):
+        for h in range(heads):
+            s = scale * (q[:, h, :] @ k[a:b, h, :].T)
+            m = np.max(s, axis=-1, keepdims=True)
+            e = np.exp(s - m)
+            z = np.sum(e, axis=-1, keepdims=True)
+            partial[r, :, h, :] = (e / z) @ v[a:b, h, :]
+            lse[r, :, h] = (m + np.log(z))[:, 0]
+    return partial, lse
+
+
+def chunk_split_attention(q, q_pos, segments, axis_dims, theta, scale, key_ranges, rows=None, q_norm=None,
+                          k_norm=None):
+    """:func:`split_attention` of the chunk's (prepared) queries over the
+    concatenated (prepared) context, key runs given in packed-row order."""
+    q = np.asarray(q, dtype=np.float64)
+    rope64.check_axis_dims(axis_dims, q.shape[-1])
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        q = q[rows]
+        if q_pos is not None:
+            q_pos = np.asarray(q_pos)[rows]
+    q = prepare(q, q_pos, q_norm, axis_dims, theta)
+    k, v = rotated_keys(segments, axis_dims, theta, k_norm=k_norm)
+    return split_attention(q, k, v, scale, key_ranges)

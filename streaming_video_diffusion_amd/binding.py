@@ -19,6 +19,7 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_ROW_ALIGN = 64
 SA_MAX_SEGMENTS = 16
+SA_MAX_SPLITS = 256
 
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
 _TORCH = {SA_F32: torch.float32, SA_BF16: torch.bfloat16}
@@ -91,6 +92,11 @@ def lib():
         L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
                                  ctypes.c_float, vp, i32, i64, i64, vp]
         L.sa_forward.restype = i32
+        L.sa_forward_split.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                       ctypes.c_float, i32, vp, vp, vp]
+        L.sa_forward_split.restype = i32
+        L.sa_combine_splits.argtypes = [i32, i64, i32, i32, vp, vp, vp, i32, i64, i64, vp]
+        L.sa_combine_splits.restype = i32
         L.sa_status_string.argtypes = [i32]
         L.sa_status_string.restype = ctypes.c_char_p
         L.sa_last_error.argtypes = []
@@ -221,4 +227,36 @@ def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None
     _check("sa_forward", lib().sa_forward(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs, _ptr(q_rope),
                                           None if qn is None else ctypes.byref(qn), float(softmax_scale),
                                           _ptr(out), _DTYPES[out.dtype], ors, ohs, _stream(stream)))
+    return out
+
+
+def sa_forward_split(ctx, q, n_splits, q_rope=None, softmax_scale=None, partial=None, lse=None, stream=None,
+                     q_norm=None):
+    """Split-KV attention: per key run, the normalised partial output float32
+    [n_splits][Nq][heads][head_dim] and the natural log-sum-exp float32
+    [n_splits][Nq][heads]. Returns (partial, lse)."""
+    qrs, qhs = _rows_heads(q, "q")
+    if softmax_scale is None:
+        softmax_scale = ctx.head_dim ** -0.5
+    nq = q.shape[0]
+    if partial is None:
+        partial = torch.empty((n_splits, nq, ctx.heads, ctx.head_dim), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((n_splits, nq, ctx.heads), dtype=torch.float32, device=q.device)
+    c = ctx.struct()
+    qn = None if q_norm is None else q_norm.struct()
+    _check("sa_forward_split", lib().sa_forward_split(ctypes.byref(c), _ptr(q), nq, qrs, qhs, _ptr(q_rope),
+                                                      None if qn is None else ctypes.byref(qn), float(softmax_scale),
+                                                      n_splits, _ptr(partial), _ptr(lse), _stream(stream)))
+    return partial, lse
+
+
+def sa_combine_splits(partial, lse, out=None, out_dtype=torch.bfloat16, stream=None):
+    """Merge split-KV results into [Nq][heads][head_dim] (LSE-weighted mean)."""
+    n_splits, nq, heads, d = partial.shape
+    if out is None:
+        out = torch.empty((nq, heads, d), dtype=out_dtype, device=partial.device)
+    ors, ohs = _rows_heads(out, "out")
+    _check("sa_combine_splits", lib().sa_combine_splits(n_splits, nq, heads, d, _ptr(partial), _ptr(lse), _ptr(out),
+                                                        _DTYPES[out.dtype], ors, ohs, _stream(stream)))
     return out

@@ -221,54 +221,128 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
     return SA_OK;
 }
 
-sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
-                     const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
-                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream) {
-    g_err[0] = 0;
+// Shared validation and argument set-up of the forward calls; out may be
+// NULL when the split-KV partial buffers take its place.
+static sa_status forward_args(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                              int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm,
+                              float softmax_scale, sa::FwdArgs &a) {
     sa_status st = check_context(ctx);
     if (st != SA_OK) return st;
     if (ctx->rows < 1) return fail(SA_ERR_CAPACITY, "ctx->rows must be >= 1 for sa_forward");
-    if (!valid_dtype(out_dtype)) return fail(SA_ERR_DTYPE, "out_dtype %d is not SA_F32 or SA_BF16", (int)out_dtype);
     if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
     if (!std::isfinite(softmax_scale)) return fail(SA_ERR_SHAPE, "softmax_scale must be finite");
-    if (nq == 0) return SA_OK;
     if (nq > (int64_t(1) << 31)) return fail(SA_ERR_SHAPE, "nq above 2^31");
-    if (!q || !out) return fail(SA_ERR_NULL, "q / out is NULL");
-    if (!aligned(q, 16) || !aligned(out, 16) || (q_rope && !aligned(q_rope, 16)))
-        return fail(SA_ERR_ALIGN, "q, out and q_rope must be 16-byte aligned");
+    if (nq > 0 && !q) return fail(SA_ERR_NULL, "q is NULL");
+    if (!aligned(q, 16) || (q_rope && !aligned(q_rope, 16)))
+        return fail(SA_ERR_ALIGN, "q and q_rope must be 16-byte aligned");
     const int64_t d = ctx->head_dim;
-    if (!stride_ok(q_row_stride, ctx->dtype) || !stride_ok(q_head_stride, ctx->dtype) ||
-        !stride_ok(o_row_stride, out_dtype) || !stride_ok(o_head_stride, out_dtype))
-        return fail(SA_ERR_ALIGN, "q / out strides must be >= 0 and keep rows 16-byte aligned");
-    if ((nq > 1 && (q_row_stride < d || o_row_stride < d)) ||
-        (ctx->heads > 1 && (q_head_stride < d || o_head_stride < d)))
-        return fail(SA_ERR_SHAPE, "a q / out stride is smaller than head_dim");
-
-    sa::FwdArgs a{};
+    if (!stride_ok(q_row_stride, ctx->dtype) || !stride_ok(q_head_stride, ctx->dtype))
+        return fail(SA_ERR_ALIGN, "q strides must be >= 0 and keep rows 16-byte aligned");
+    if ((nq > 1 && q_row_stride < d) || (ctx->heads > 1 && q_head_stride < d))
+        return fail(SA_ERR_SHAPE, "a q stride is smaller than head_dim");
+    a = sa::FwdArgs{};
     st = check_norm(q_norm, "q_norm", a.q_norm);
     if (st != SA_OK) return st;
     a.q = q;
     a.q_rope = q_rope;
     a.k = ctx->k_packed;
     a.v = ctx->v_packed;
-    a.out = out;
     a.q_rs = q_row_stride;
     a.q_hs = q_head_stride;
-    a.o_rs = o_row_stride;
-    a.o_hs = o_head_stride;
     a.nq = nq;
     a.nk = ctx->rows;
     a.cap = ctx->capacity_rows;
     a.heads = ctx->heads;
-    a.out_f32 = out_dtype == SA_F32;
     a.scale = softmax_scale;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    a.n_splits = 1;
+    return SA_OK;
+}
+
+static sa_status forward_launch(const sa_context *ctx, sa::FwdArgs &a, hipStream_t stream) {
     const int64_t rows_per_wg = ctx->dtype == SA_BF16 ? sa::fwd_bf16_rows_per_workgroup() : sa::kFwdF32RowsPerWorkgroup;
-    const int64_t blocks = ((nq + rows_per_wg - 1) / rows_per_wg) * ctx->heads;
-    if (blocks > 0x7fffffff) return fail(SA_ERR_SHAPE, "nq x heads too large for one grid");
+    const int64_t blocks = ((a.nq + rows_per_wg - 1) / rows_per_wg) * ctx->heads * a.n_splits;
+    if (blocks > 0x7fffffff) return fail(SA_ERR_SHAPE, "nq x heads x splits too large for one grid");
     hipError_t e = ctx->dtype == SA_BF16 ? sa::launch_fwd_bf16(a, ctx->head_dim, stream)
                                          : sa::launch_fwd_f32(a, ctx->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return SA_OK;
+}
+
+sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
+                     const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
+                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, a);
+    if (st != SA_OK) return st;
+    if (!valid_dtype(out_dtype)) return fail(SA_ERR_DTYPE, "out_dtype %d is not SA_F32 or SA_BF16", (int)out_dtype);
+    if (nq == 0) return SA_OK;
+    if (!out) return fail(SA_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(SA_ERR_ALIGN, "out must be 16-byte aligned");
+    const int64_t d = ctx->head_dim;
+    if (!stride_ok(o_row_stride, out_dtype) || !stride_ok(o_head_stride, out_dtype))
+        return fail(SA_ERR_ALIGN, "out strides must be >= 0 and keep rows 16-byte aligned");
+    if ((nq > 1 && o_row_stride < d) || (ctx->heads > 1 && o_head_stride < d))
+        return fail(SA_ERR_SHAPE, "an out stride is smaller than head_dim");
+    a.out = out;
+    a.o_rs = o_row_stride;
+    a.o_hs = o_head_stride;
+    a.out_f32 = out_dtype == SA_F32;
+    return forward_launch(ctx, a, stream);
+}
+
+sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                           int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                           int32_t n_splits, float *partial, float *lse, hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, a);
+    if (st != SA_OK) return st;
+    const int64_t ntiles = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN;
+    if (n_splits < 1 || n_splits > SA_MAX_SPLITS || n_splits > ntiles)
+        return fail(SA_ERR_SHAPE, "n_splits %d outside [1, min(%d, %lld key tiles)]", n_splits, SA_MAX_SPLITS,
+                    (long long)ntiles);
+    if (nq == 0) return SA_OK;
+    if (!partial || !lse) return fail(SA_ERR_NULL, "partial / lse is NULL");
+    if (!aligned(partial, 16) || !aligned(lse, 4)) return fail(SA_ERR_ALIGN, "partial must be 16-byte aligned");
+    a.n_splits = n_splits;
+    a.partial = partial;
+    a.lse = lse;
+    a.out_f32 = 1;
+    return forward_launch(ctx, a, stream);
+}
+
+sa_status sa_combine_splits(int32_t n_splits, int64_t nq, int32_t heads, int32_t head_dim, const float *partial,
+                            const float *lse, void *out, sa_dtype out_dtype, int64_t o_row_stride,
+                            int64_t o_head_stride, hipStream_t stream) {
+    g_err[0] = 0;
+    if (n_splits < 1 || n_splits > SA_MAX_SPLITS) return fail(SA_ERR_SHAPE, "n_splits %d outside [1, %d]", n_splits, SA_MAX_SPLITS);
+    if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
+    if (heads < 1 || heads > 65535) return fail(SA_ERR_SHAPE, "heads %d outside [1, 65535]", heads);
+    if (!supported_dim(head_dim)) return fail(SA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (!valid_dtype(out_dtype)) return fail(SA_ERR_DTYPE, "out_dtype %d is not SA_F32 or SA_BF16", (int)out_dtype);
+    if (nq == 0) return SA_OK;
+    if (nq * heads > (int64_t(1) << 33)) return fail(SA_ERR_SHAPE, "nq x heads too large");
+    if (!partial || !lse || !out) return fail(SA_ERR_NULL, "partial / lse / out is NULL");
+    if (!aligned(partial, 16) || !aligned(lse, 4) || !aligned(out, 16))
+        return fail(SA_ERR_ALIGN, "partial and out must be 16-byte aligned");
+    if (!stride_ok(o_row_stride, out_dtype) || !stride_ok(o_head_stride, out_dtype))
+        return fail(SA_ERR_ALIGN, "out strides must be >= 0 and keep rows 16-byte aligned");
+    if ((nq > 1 && o_row_stride < head_dim) || (heads > 1 && o_head_stride < head_dim))
+        return fail(SA_ERR_SHAPE, "an out stride is smaller than head_dim");
+    sa::CombineArgs a{};
+    a.partial = partial;
+    a.lse = lse;
+    a.out = out;
+    a.nq = nq;
+    a.o_rs = o_row_stride;
+    a.o_hs = o_head_stride;
+    a.heads = heads;
+    a.n_splits = n_splits;
+    a.out_f32 = out_dtype == SA_F32;
+    hipError_t e = sa::launch_combine(a, head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
     return SA_OK;
 }
 

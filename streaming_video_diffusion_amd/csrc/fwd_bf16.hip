@@ -168,8 +168,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int per = nwg >> 3, rem = nwg & 7;
     const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
     const int n_qt = (int)((a.nq + BM - 1) / BM);
-    const int head = logical / n_qt;
-    const int qt = logical - head * n_qt;
+    // logical = (head * n_splits + split) * n_qt + query tile: the workgroups
+    // of one head and key range are neighbours, so they share an XCD's L2.
+    const int hs = logical / n_qt;
+    const int qt = logical - hs * n_qt;
+    const int head = hs / a.n_splits;
+    const int split = hs - head * a.n_splits;
 
     const int t = threadIdx.x;
     const int w = t >> 6;
@@ -241,8 +245,11 @@ void fwd_bf16_kernel(FwdArgs a) {
 
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)head * a.cap * D * 2;
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(a.v) + (int64_t)head * D * a.cap * 2;
-    const int ntiles = (int)((a.nk + BN - 1) / BN);
+    const int ntiles_all = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
+    // This workgroup's key tiles [t_begin, ntiles) (all of them without split-KV).
+    const int t_begin = split_first_tile(split, a.n_splits, ntiles_all);
+    const int ntiles = split_first_tile(split + 1, a.n_splits, ntiles_all);
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     const f32x16 zero16 = f32x16{};
     const uint32_t A0 = T::kbase(l32, hf);
@@ -280,7 +287,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     };
     // Keys >= nk of the last tile get -inf scores.
     auto mask = [&](f32x16 (&s)[2], int kt) __attribute__((always_inline)) {
-        if (ragged && kt + 1 == ntiles) {
+        if (ragged && kt + 1 == ntiles_all) {
             // key (tile-relative) = 32 tt + 8 (i / 4) + 4 hf + i % 4 is masked when >= nk - k0
             const int lim = (int)(a.nk - (int64_t)kt * BN) - 4 * hf;
 #pragma unroll
@@ -394,8 +401,25 @@ void fwd_bf16_kernel(FwdArgs a) {
 
     // Output of this lane's half of row q_row: O^T column l32, d-rows
     // 32 c + 8 g + 4 hf .. +3 of each 32-row d tile.
-    auto store = [&](float lsum) __attribute__((always_inline)) {
+    auto store = [&](float lsum, float m) __attribute__((always_inline)) {
         const float inv = 1.0f / lsum;
+        if (a.partial) {  // split-KV: normalised partial output and natural log-sum-exp
+            const int64_t prow = ((int64_t)split * a.nq + q_row) * a.heads + head;
+            float *pp = a.partial + prow * D;
+#pragma unroll
+            for (int c = 0; c < DT; ++c)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 r;
+                    r.x = o[c][4 * g + 0] * inv;
+                    r.y = o[c][4 * g + 1] * inv;
+                    r.z = o[c][4 * g + 2] * inv;
+                    r.w = o[c][4 * g + 3] * inv;
+                    *reinterpret_cast<f32x4 *>(pp + 32 * c + 8 * g + 4 * hf) = r;
+                }
+            if (hf == 0) a.lse[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
+            return;
+        }
         const int64_t obase = q_row * a.o_rs + (int64_t)head * a.o_hs;
 #pragma unroll
         for (int c = 0; c < DT; ++c)
@@ -429,12 +453,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     // second pass below with an explicit running max. While the softmax of tile
     // kt runs on the VALU, the matrix cores already form the scores of tile
     // kt+1.
-    issue(0);
-    issue(1);
+    issue(t_begin);
+    issue(t_begin + 1);
     end_tile();
     f32x16 s[2];
-    qk(buf_of(0), s, zero16);
-    for (int kt = 0; kt < ntiles; ++kt) {
+    qk(buf_of(t_begin), s, zero16);
+    for (int kt = t_begin; kt < ntiles; ++kt) {
         // On the last tile the next-tile scores read a resident buffer and are
         // discarded.
         issue(kt + 2);
@@ -461,7 +485,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     osum += half_swap_partner(osum);
     const bool row = q_row < a.nq;
     const bool ok = lt >= 0x1p-100f && lt <= 0x1p+100f && __builtin_isfinite(osum);
-    if (row && ok) store(lt);
+    if (row && ok) store(lt, 0.0f);
 
     // ---- second pass (rare): explicit running max ---------------------------
     // Taken by the whole workgroup when any of its rows failed the check;
@@ -486,20 +510,20 @@ void fwd_bf16_kernel(FwdArgs a) {
         for (int c = 0; c < DT; ++c) o[c] = f32x16{};
         l = 0.f;
         float m = 0.f;
-        issue(0);
-        issue(1);
+        issue(t_begin);
+        issue(t_begin + 1);
         end_tile();
-        for (int kt = 0; kt < ntiles; ++kt) {
+        for (int kt = t_begin; kt < ntiles; ++kt) {
             issue(kt + 2);
             qk(buf_of(kt), s, zero16);
             mask(s, kt);
             const float mx = tile_max(s);  // absolute tile max (log2 units)
             float mnew;
-            if (kt == 0)  // nothing accumulated yet: adopt the first tile's max if out of band
+            if (kt == t_begin)  // nothing accumulated yet: adopt the first tile's max if out of band
                 mnew = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
             else
                 mnew = (mx - m > kLazyRescale) ? mx : m;
-            const float alpha = kt == 0 ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+            const float alpha = kt == t_begin ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
             l *= alpha;
 #pragma unroll
             for (int c = 0; c < DT; ++c) o[c] *= alpha;
@@ -508,7 +532,7 @@ void fwd_bf16_kernel(FwdArgs a) {
             end_tile();
         }
         lt = l + half_swap_partner(l);
-        if (row && !ok) store(lt);
+        if (row && !ok) store(lt, m);
     }
 }
 
@@ -521,7 +545,7 @@ template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     constexpr int BM = kNW * 32;
     const int64_t n_qt = (a.nq + BM - 1) / BM;
-    const int64_t nwg = n_qt * a.heads;
+    const int64_t nwg = n_qt * a.heads * a.n_splits;
     auto kern = fwd_bf16_kernel<D, kNW, OUT_F32>;
     constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,

@@ -26,8 +26,15 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     __shared__ __align__(16) float sv[kTN * D];
 
     const int n_qt = (int)((a.nq + kQ - 1) / kQ);
-    const int head = blockIdx.x / n_qt;
-    const int qt = blockIdx.x - head * n_qt;
+    const int hs = blockIdx.x / n_qt;  // head * n_splits + split
+    const int qt = blockIdx.x - hs * n_qt;
+    const int head = hs / a.n_splits;
+    const int split = hs - head * a.n_splits;
+    // this workgroup's keys: whole 64-key tiles of its split (all keys without split-KV)
+    const int ntiles_all = (int)((a.nk + 63) / 64);
+    const int64_t k_begin = (int64_t)split_first_tile(split, a.n_splits, ntiles_all) * 64;
+    const int64_t k_end_t = (int64_t)split_first_tile(split + 1, a.n_splits, ntiles_all) * 64;
+    const int64_t k_end = k_end_t < a.nk ? k_end_t : a.nk;
     const int t = threadIdx.x;
     const int half = t & 1;
     const int64_t row = (int64_t)qt * kQ + (t >> 1);
@@ -80,8 +87,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
     const float *kb = reinterpret_cast<const float *>(a.k) + (int64_t)head * a.cap * D;
     const float *vb = reinterpret_cast<const float *>(a.v) + (int64_t)head * a.cap * D;
-    for (int64_t k0 = 0; k0 < a.nk; k0 += kTN) {
-        const int nt = (int)((a.nk - k0) < kTN ? (a.nk - k0) : kTN);
+    for (int64_t k0 = k_begin; k0 < k_end; k0 += kTN) {
+        const int nt = (int)((k_end - k0) < kTN ? (k_end - k0) : kTN);
         for (int id = t; id < kTN * D / 4; id += kThreads) {
             const int r = id / (D / 4), ch = id % (D / 4);
             f32x4 kv = f32x4{}, vv = f32x4{};
@@ -122,6 +129,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
     if (!valid) return;
     const float inv = 1.0f / l;
+    if (a.partial) {  // split-KV: normalised partial output and natural log-sum-exp
+        const int64_t prow = ((int64_t)split * a.nq + row) * a.heads + head;
+        float *pp = a.partial + prow * D + half * H2;
+#pragma unroll
+        for (int e = 0; e < H2; ++e) pp[e] = o[e] * inv;
+        if (half == 0) a.lse[prow] = m + logf(l);
+        return;
+    }
     const int64_t obase = row * a.o_rs + (int64_t)head * a.o_hs + half * H2;
     if (OUT_F32) {
         float *op = reinterpret_cast<float *>(a.out) + obase;
@@ -149,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     const int64_t n_qt = (a.nq + kQ - 1) / kQ;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), dim3((unsigned)(n_qt * a.heads)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), dim3((unsigned)(n_qt * a.heads * a.n_splits)), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

@@ -74,7 +74,25 @@ struct FwdArgs {
     float scale;       // softmax scale
     float scale_log2;  // softmax scale * log2(e)
     NormArgs q_norm;
+    // Split-KV: n_splits >= 1 contiguous runs of 64-key tiles; with partial
+    // set, each workgroup writes its run's normalised output, float32
+    // [split][nq][heads][d], and natural log-sum-exp, float32 [split][nq][heads].
+    int32_t n_splits;
+    float *partial;
+    float *lse;
 };
+// Key tiles [first, end) of split s of n over ntiles tiles (balanced, non-empty when n <= ntiles).
+__host__ __device__ inline int split_first_tile(int s, int n, int ntiles) { return (int)((int64_t)s * ntiles / n); }
+
+// --- split-KV combine -------------------------------------------------------
+struct CombineArgs {
+    const float *partial;  // [n_splits][nq][heads][d]
+    const float *lse;      // [n_splits][nq][heads]
+    void *out;
+    int64_t nq, o_rs, o_hs;
+    int32_t heads, n_splits, out_f32;
+};
+hipError_t launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream);
 int fwd_bf16_rows_per_workgroup();  // query rows one bf16 forward workgroup owns
 constexpr int kFwdF32RowsPerWorkgroup = 64;

@@ -321,7 +321,37 @@ def pin_qknorm_then_rotation():
     _close(got, ref, 1e-13, "norm then rotation, one pair")
 
 
+def pin_split_lse_closed_forms():
+    """One key: lse = the scaled score and the partial = v; two keys: log(e^a + e^b);
+    many keys: scipy's logsumexp of the fp64 scores."""
+    from scipy.special import logsumexp
+    rng = _rng(121)
+    q = rng.standard_normal((3, 2, 8))
+    k = rng.standard_normal((5, 2, 8))
+    v = rng.standard_normal((5, 2, 8))
+    part, lse = attn64.split_attention(q, k, v, 0.7, [(2, 3), (3, 5), (0, 5)])
+    s = 0.7 * np.einsum("nhd,jhd->nhj", q, k)
+    _close(lse[0], s[:, :, 2], 1e-14, "lse of one key")
+    _close(part[0], np.broadcast_to(v[2], part[0].shape), 1e-14, "one key returns its value")
+    _close(lse[1], np.log(np.exp(s[:, :, 3]) + np.exp(s[:, :, 4])), 1e-13, "lse of two keys")
+    _close(lse[2], logsumexp(s, axis=-1), 1e-13, "lse vs scipy logsumexp")
+
+
+def pin_split_merge_identity():
+    """Merging disjoint runs, each weighted by exp(its lse), gives the full
+    softmax attention (the identity split-key evaluation rests on)."""
+    q, qp, segs = _tiny_case(122, 64, (16, 24, 24), 2, [40, 23], 6, prompt=3)
+    scale = 0.125
+    full = attn64.chunk_attention(q, qp, segs, (16, 24, 24), THETA, scale)
+    ranges = [(0, 10), (10, 11), (11, 40), (40, 66)]
+    part, lse = attn64.chunk_split_attention(q, qp, segs, (16, 24, 24), THETA, scale, ranges)
+    w = np.exp(lse - lse.max(axis=0, keepdims=True))
+    merged = np.einsum("snh,snhd->nhd", w, part) / w.sum(axis=0)[:, :, None]
+    _close(merged, full, 1e-13, "split merge identity")
+
+
 ALL_PINS = [pin_brute_force, pin_rotation_closed_form, pin_rotation_group, pin_single_pair_scores,
             pin_softmax_rows, pin_constant_v, pin_joint_permutation, pin_zero_angle_is_sdpa,
             pin_two_keys, pin_degenerate, pin_translation, pin_row_selection, pin_rmsnorm_closed_form,
-            pin_rmsnorm_invariants, pin_brute_force_qknorm, pin_qknorm_then_rotation]
+            pin_rmsnorm_invariants, pin_brute_force_qknorm, pin_qknorm_then_rotation, pin_split_lse_closed_forms,
+            pin_split_merge_identity]

@@ -196,3 +196,37 @@ def test_forward_errors(L):
     # nq == 0 enqueues nothing and succeeds
     assert fwd(L, ctx(), nq=0) == 0
     assert L.sa_last_error() == b""
+
+
+def fwd_split(L, c, nsplit=2, q=FAKE, nq=8, partial=FAKE * 4, lse=FAKE * 5, qrs=256, qhs=128):
+    return L.sa_forward_split(ctypes.byref(c), q, nq, qrs, qhs, None, None, 0.1, nsplit, partial, lse, None)
+
+
+def test_forward_split_errors(L):
+    c = ctx(rows=128, capacity_rows=128)   # two key tiles
+    assert fwd_split(L, c, nsplit=0) == ERR["SHAPE"]
+    assert fwd_split(L, c, nsplit=3) == ERR["SHAPE"]       # more splits than key tiles
+    assert fwd_split(L, ctx(rows=20000, capacity_rows=20032), nsplit=257) == ERR["SHAPE"]
+    assert fwd_split(L, c, partial=None) == ERR["NULL"]
+    assert fwd_split(L, c, lse=None) == ERR["NULL"]
+    assert fwd_split(L, c, partial=FAKE + 4) == ERR["ALIGN"]
+    assert fwd_split(L, c, q=FAKE + 2) == ERR["ALIGN"]
+    assert fwd_split(L, c, qhs=64) == ERR["SHAPE"]
+    assert fwd_split(L, ctx(rows=0)) == ERR["CAPACITY"]
+    assert fwd_split(L, c, nq=0, partial=None, lse=None) == 0
+
+
+def test_combine_errors(L):
+    def comb(ns=2, nq=8, heads=2, d=128, partial=FAKE, lse=FAKE * 2, out=FAKE * 3, odt=B.SA_BF16, ors=256, ohs=128):
+        return L.sa_combine_splits(ns, nq, heads, d, partial, lse, out, odt, ors, ohs, None)
+    assert comb(ns=0) == ERR["SHAPE"]
+    assert comb(ns=257) == ERR["SHAPE"]
+    assert comb(nq=-1) == ERR["SHAPE"]
+    assert comb(heads=0) == ERR["SHAPE"]
+    assert comb(d=96) == ERR["UNSUPPORTED"]
+    assert comb(odt=4) == ERR["DTYPE"]
+    assert comb(partial=None) == ERR["NULL"]
+    assert comb(out=FAKE + 2) == ERR["ALIGN"]
+    assert comb(ors=96) == ERR["SHAPE"]
+    assert comb(ors=250) == ERR["ALIGN"]
+    assert comb(nq=0, partial=None) == 0
