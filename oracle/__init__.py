@@ -12,6 +12,8 @@ What it computes is the plain definition of the operation, in float64:
   positions and the per-pair rotation.
 * ``norm64``  -- per-head RMS normalisation of queries and keys (QK-norm),
   applied before the rotation.
+* ``pool64``  -- s x s spatial mean pooling of aged history frames into a
+  coarser tier (of keys before their normalisation and rotation, and of values).
 * ``attn64``  -- dense softmax attention of the current chunk's queries over the
   concatenated key/value context (prompt KV | reference frame | history tiers |
   current chunk), vectorised with numpy per head and query block.
@@ -31,6 +33,6 @@ invariants, a library routine (SDPA) and brute force; nothing is "parity
 unpinned".
 """
 
-from . import rope64, norm64, attn64, brute  # noqa: F401
+from . import rope64, norm64, pool64, attn64, brute  # noqa: F401
 
-__all__ = ["rope64", "norm64", "attn64", "brute"]
+__all__ = ["rope64", "norm64", "pool64", "attn64", "brute"]

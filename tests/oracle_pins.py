@@ -20,7 +20,7 @@ import math
 import numpy as np
 import torch
 
-from oracle import attn64, brute, norm64, rope64
+from oracle import attn64, brute, norm64, pool64, rope64
 
 AX128 = (32, 48, 48)
 THETA = 10000.0
@@ -350,8 +350,84 @@ def pin_split_merge_identity():
     _close(merged, full, 1e-13, "split merge identity")
 
 
+def _pool_loops(x, grid_h, grid_w, s):
+    """Scalar twin of the pooling: every output element as an fsum over its
+    s*s source rows, addressed by flat row index."""
+    x = np.asarray(x, dtype=np.float64)
+    n, heads, d = x.shape
+    per = grid_h * grid_w
+    ph, pw = grid_h // s, grid_w // s
+    out = np.zeros((n // per * ph * pw, heads, d))
+    for f in range(n // per):
+        for i in range(ph):
+            for j in range(pw):
+                src = [f * per + (s * i + a) * grid_w + (s * j + b) for a in range(s) for b in range(s)]
+                for h in range(heads):
+                    for c in range(d):
+                        out[(f * ph + i) * pw + j, h, c] = math.fsum(x[r, h, c] for r in src) / (s * s)
+    return out
+
+
+def pin_pool_brute_force():
+    """Pooling == scalar loops over a non-square grid (2 frames, 4 x 8 cells), s = 2 and 4."""
+    rng = _rng(130)
+    x = rng.standard_normal((2 * 4 * 8, 2, 3))
+    for s in (2, 4):
+        _close(pool64.pool_frames(x, 4, 8, s), _pool_loops(x, 4, 8, s), 1e-14, f"pool s={s}")
+
+
+def pin_pool_closed_forms():
+    """A frame whose value is a*h + b*w + c (h = grid row, w = column) pools to
+    a*hc + b*wc + c at the cell centre hc = s*i + (s-1)/2, wc = s*j + (s-1)/2;
+    s = 1 is the identity; frames stay separate (no pooling over time)."""
+    gh, gw = 4, 8
+    h, w = np.meshgrid(np.arange(gh), np.arange(gw), indexing="ij")
+    frames = [3.0 * h - 0.5 * w + 1.0, -2.0 * h + 7.0 * w - 4.0]
+    x = np.stack([f.reshape(-1) for f in frames]).reshape(-1)[:, None, None]
+    rng = _rng(131)
+    y = rng.standard_normal((2 * gh * gw, 1, 4))
+    _close(pool64.pool_frames(y, gh, gw, 1), y, 0.0, "s = 1 is the identity")
+    for s in (2, 4):
+        hc, wc = np.meshgrid(np.arange(gh // s) * s + (s - 1) / 2, np.arange(gw // s) * s + (s - 1) / 2,
+                             indexing="ij")
+        want = np.concatenate([(3.0 * hc - 0.5 * wc + 1.0).reshape(-1), (-2.0 * hc + 7.0 * wc - 4.0).reshape(-1)])
+        _close(pool64.pool_frames(x, gh, gw, s)[:, 0, 0], want, 1e-15, f"affine frame, s={s}")
+
+
+def pin_pool_invariants():
+    """Pooling keeps each frame's mean, is linear, and 2x2 of 2x2 equals 4x4."""
+    rng = _rng(132)
+    gh, gw = 8, 12
+    x = rng.standard_normal((3 * gh * gw, 2, 5))
+    y = rng.standard_normal(x.shape)
+    p4 = pool64.pool_frames(x, gh, gw, 4)
+    _close(p4.reshape(3, -1, 2, 5).mean(axis=1), x.reshape(3, -1, 2, 5).mean(axis=1), 1e-14, "frame mean")
+    _close(pool64.pool_frames(2.0 * x - 3.0 * y, gh, gw, 2),
+           2.0 * pool64.pool_frames(x, gh, gw, 2) - 3.0 * pool64.pool_frames(y, gh, gw, 2), 1e-14, "linear")
+    _close(pool64.pool_frames(pool64.pool_frames(x, gh, gw, 2), gh // 2, gw // 2, 2), p4, 1e-14, "2x2 of 2x2")
+
+
+def pin_pooled_tier_attention():
+    """Attention over a pooled tier == brute force over the hand-pooled keys and
+    values at the cell-centre positions (pool first, then rotate)."""
+    rng = _rng(133)
+    d, ax, gh, gw, s = 8, (2, 2, 4), 4, 4, 2
+    k = rng.standard_normal((2 * gh * gw, 1, d))
+    v = rng.standard_normal((2 * gh * gw, 1, d))
+    pos = np.array([[t, (s * i + (s - 1) / 2), (s * j + (s - 1) / 2)]
+                    for t in (1, 2) for i in range(gh // s) for j in range(gw // s)], dtype=np.float64)
+    q = rng.standard_normal((3, 1, d))
+    qp = rng.random((3, 3)) * 5.0
+    got = attn64.chunk_attention(q, qp, [(pool64.pool_frames(k, gh, gw, s), pool64.pool_frames(v, gh, gw, s), pos)],
+                                 ax, THETA, 0.4)
+    kp, vp = _pool_loops(k, gh, gw, s), _pool_loops(v, gh, gw, s)
+    ref = brute.chunk_attention(q, qp, [(kp, vp, pos)], ax, THETA, 0.4)
+    _close(got, ref, 1e-12, "pooled tier attention")
+
+
 ALL_PINS = [pin_brute_force, pin_rotation_closed_form, pin_rotation_group, pin_single_pair_scores,
             pin_softmax_rows, pin_constant_v, pin_joint_permutation, pin_zero_angle_is_sdpa,
             pin_two_keys, pin_degenerate, pin_translation, pin_row_selection, pin_rmsnorm_closed_form,
             pin_rmsnorm_invariants, pin_brute_force_qknorm, pin_qknorm_then_rotation, pin_split_lse_closed_forms,
-            pin_split_merge_identity]
+            pin_split_merge_identity, pin_pool_brute_force, pin_pool_closed_forms, pin_pool_invariants,
+            pin_pooled_tier_attention]

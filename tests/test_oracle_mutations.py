@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle_pins
-from oracle import attn64, norm64, rope64
+from oracle import attn64, norm64, pool64, rope64
 
 
 def _rotate_with(fn):
@@ -113,7 +113,46 @@ def _prepare_norm_ignored(x, pos, norm, axis_dims, theta):
     return x
 
 
+def _pool_with(reduce, order_hw=True, swap_grid=False):
+    def pool_frames(x, grid_h, grid_w, s):
+        x = np.asarray(x, dtype=np.float64)
+        if swap_grid:
+            grid_h, grid_w = grid_w, grid_h
+        frames = x.shape[0] // (grid_h * grid_w)
+        rest = x.shape[1:]
+        b = reduce(x.reshape((frames, grid_h // s, s, grid_w // s, s) + rest))
+        if not order_hw:
+            b = np.swapaxes(b, 1, 2)
+        return b.reshape((frames * (grid_h // s) * (grid_w // s),) + rest)
+    return pool_frames
+
+
+def _split_with(lse_form, normalise=True):
+    def split_attention(q, k, v, scale, key_ranges):
+        q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+        nq, heads, d = q.shape
+        partial = np.empty((len(key_ranges), nq, heads, d))
+        lse = np.empty((len(key_ranges), nq, heads))
+        for r, (a, b) in enumerate(key_ranges):
+            for h in range(heads):
+                sc = scale * (q[:, h, :] @ k[a:b, h, :].T)
+                m = np.max(sc, axis=-1, keepdims=True)
+                e = np.exp(sc - m)
+                z = np.sum(e, axis=-1, keepdims=True)
+                partial[r, :, h, :] = ((e / z) if normalise else e) @ v[a:b, h, :]
+                lse[r, :, h] = lse_form(m, z)[:, 0]
+        return partial, lse
+    return split_attention
+
+
 MUTATIONS = {
+    "pool_sum_not_mean": [(pool64, "pool_frames", _pool_with(lambda b: b.sum(axis=(2, 4))))],
+    "pool_first_cell_only": [(pool64, "pool_frames", _pool_with(lambda b: b[:, :, 0, :, 0]))],
+    "pool_cells_column_major": [(pool64, "pool_frames", _pool_with(lambda b: b.mean(axis=(2, 4)), order_hw=False))],
+    "pool_grid_transposed": [(pool64, "pool_frames", _pool_with(lambda b: b.mean(axis=(2, 4)), swap_grid=True))],
+    "split_lse_log2": [(attn64, "split_attention", _split_with(lambda m, z: m + np.log2(z)))],
+    "split_lse_no_max": [(attn64, "split_attention", _split_with(lambda m, z: np.log(z)))],
+    "split_partial_unnormalised": [(attn64, "split_attention", _split_with(lambda m, z: m + np.log(z), False))],
     "rms_sum_not_mean": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.sqrt(np.sum(x * x, -1, keepdims=True) + e)))],
     "rms_no_sqrt": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.mean(x * x, -1, keepdims=True) + e))],
     "rms_eps_outside_sqrt": [(norm64, "rmsnorm", _rms_with(lambda x, e: np.sqrt(np.mean(x * x, -1, keepdims=True)) + e))],
