@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--qk-norm", action="store_true",
                    help="fuse per-head RMS QK-norm (shared weights) into the pack and the query load")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the forward times of the other workloads and query variants")
     p.add_argument("--no-shard", action="store_true",
                    help="skip the extra measurement of one GPU's head shard (40/8 = 5 heads)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -146,6 +148,59 @@ def shard_measure(steps):
     return {"heads": 5, "nq": w.nq, "nk": w.nk, "forward_ms": ms,
             "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12,
             "workgroups": ((w.nq + 255) // 256) * w.heads}
+
+
+def _time(fn, stream, steps):
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def other_workloads(steps, skip):
+    """Forward time of the other 1344x768 workloads (hierarchical history,
+    joint video+audio, and the query-side variants: history + current as
+    queries, the 7-frame first window, the prefix self-attention pass), and
+    the 40 audio-only queries of the video+audio chunk run over 32 key splits
+    + merge vs one plain forward. Extra lines, not the metric."""
+    import torch
+    from streaming_video_diffusion_amd import binding as B
+    from streaming_video_diffusion_amd import inputs as I
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    stream = torch.cuda.current_stream()
+    res = {}
+    makers = [f for n, f in list(I.CONFIGS.items()) + list(I.VARIANTS.items())
+              if n != skip and f().nq >= 4096]
+    for make in makers:
+        w = make()
+        ca = ChunkAttention(w, device="cuda:0")
+        ca.pack_static(stream)
+        ca.step(stream)
+        ms = _time(lambda: ca.forward(stream), stream, steps)
+        res[w.name] = {"nq": w.nq, "nk": w.nk, "forward_ms": ms,
+                       "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12}
+        if w.name == "video_audio_1344x768":
+            q, qt = ca.q[w.nq - 40:], ca.q_table[w.nq - 40:]
+            out = torch.empty((40, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
+            part = torch.empty((32, 40, w.heads, w.head_dim), dtype=torch.float32, device="cuda:0")
+            lse = torch.empty((32, 40, w.heads), dtype=torch.float32, device="cuda:0")
+
+            def split():
+                B.sa_forward_split(ca.ctx, q, 32, qt, w.scale, partial=part, lse=lse, stream=stream)
+                B.sa_combine_splits(part, lse, out=out, stream=stream)
+
+            plain = _time(lambda: B.sa_forward(ca.ctx, q, qt, w.scale, out=out, stream=stream), stream, steps)
+            res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps)}
+        del ca
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -246,6 +301,8 @@ def main():
     }
     if not args.no_shard:
         out["one_gpu_head_shard"] = shard_measure(20)
+    if not args.no_others:
+        out["other_workloads"] = other_workloads(10, w.name)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -220,6 +220,42 @@ CONFIGS = {w().name: w for w in (tiny_f32, lowres_bf16, full_1344x768, hier_1344
                                  video_audio_1344x768)}
 
 
+# Query-side variants on the same kernel (StreamRender-H3 page, streaming-context
+# section): at inference the recent history is recomputed together with the
+# current chunk; the first window, having no earlier context, generates seven
+# scheduling units at once; the fixed prefix (conditions, reference, sink)
+# attends only to itself when its key/values are computed. One scheduling unit
+# is read as one latent frame (the page gives one to two) and the sink as two
+# units, as in the deployed model the page describes.
+
+def history_query_1344x768():
+    """Recomputed history + current chunk as queries over the 1344x768 context."""
+    segs, cur = _video_segments(256, 48, 84, 0, [("history", [1, 2, 3], 1)], [4, 5, 6])
+    q_pos = np.concatenate([segs[2].pos, cur])
+    return Workload("history_query_1344x768", 6, "bf16", 40, 128, q_pos, segs,
+                    description="1344x768 history+current as queries: 24192 q x 28480 kv, 40 heads, d128")
+
+
+def first_window_1344x768():
+    """First window: seven latent frames generated at once over prompt + reference + themselves."""
+    segs, cur = _video_segments(256, 48, 84, 0, [], [1, 2, 3, 4, 5, 6, 7])
+    return Workload("first_window_1344x768", 7, "bf16", 40, 128, cur, segs,
+                    description="1344x768 first window: 28224 q x 32512 kv, 40 heads, d128")
+
+
+def prefix_self_1344x768():
+    """Prefix pass: reference + two sink frames attend to prompt + themselves only."""
+    segs = [Segment("prompt", 256, None, False),
+            Segment("ref", 4032, frame_positions([0], 48, 84), False),
+            Segment("sink", 8064, frame_positions([1, 2], 48, 84), False)]
+    q_pos = np.concatenate([segs[1].pos, segs[2].pos])
+    return Workload("prefix_self_1344x768", 8, "bf16", 40, 128, q_pos, segs,
+                    description="1344x768 prefix self-attention: 12096 q x 12352 kv, 40 heads, d128")
+
+
+VARIANTS = {w().name: w for w in (history_query_1344x768, first_window_1344x768, prefix_self_1344x768)}
+
+
 def custom(name, cfg_id, dtype, heads, head_dim, seg_rows, nq, rotary=True, prompt_rows=0,
            pos_scale=40.0, axis_dims=None, theta=ROPE_THETA, scale=None, qk_norm=None):
     """Arbitrary-shape workload for tests: random positions, given row counts.

@@ -47,8 +47,10 @@ class ChunkAttention:
         row = 0
         for i, s in enumerate(w.segments):
             k, v = w.kv(i, call)
-            shares_q = (s.pos is not None and w.q_pos is not None and s.pos.shape == w.q_pos.shape
-                        and np.array_equal(s.pos, w.q_pos))
+            # A dynamic segment at exactly the query positions reuses the query table
+            # (built with the dynamic tables; static segments are packed before it).
+            shares_q = (s.dynamic and s.pos is not None and w.q_pos is not None
+                        and s.pos.shape == w.q_pos.shape and np.array_equal(s.pos, w.q_pos))
             pos = None
             table = None
             if s.pos is not None and not shares_q and s.rows > 0:

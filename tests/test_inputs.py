@@ -65,3 +65,31 @@ def test_draws_are_seeded_and_distinct():
     ss = [np.random.SeedSequence([I.ENTROPY, 5, c, 0]).generate_state(2).tolist() for c in (0, 1)]
     assert ss[0] != ss[1]
     assert abs(float(a.std()) - 1.0) < 0.02
+
+
+def test_query_variants():
+    """Recomputed history + current as queries, the 7-frame first window, the prefix pass."""
+    hq = I.history_query_1344x768()
+    assert (hq.nq, hq.nk) == (24192, 28480)
+    np.testing.assert_array_equal(hq.q_pos[:12096], hq.segments[2].pos)
+    np.testing.assert_array_equal(hq.q_pos[12096:], hq.segments[3].pos)
+    fw = I.first_window_1344x768()
+    assert (fw.nq, fw.nk) == (7 * 4032, 256 + 4032 + 7 * 4032)
+    assert fw.q_pos[0, 0] == 1 and fw.q_pos[-1].tolist() == [7, 47, 83]
+    assert np.array_equal(fw.segments[-1].pos, fw.q_pos) and fw.segments[-1].dynamic
+    ps = I.prefix_self_1344x768()
+    assert (ps.nq, ps.nk) == (3 * 4032, 256 + 3 * 4032)
+    assert not any(s.dynamic for s in ps.segments)
+    np.testing.assert_array_equal(ps.q_pos, np.concatenate([ps.segments[1].pos, ps.segments[2].pos]))
+    ids = {w().cfg_id for w in list(I.CONFIGS.values()) + list(I.VARIANTS.values())}
+    assert len(ids) == len(I.CONFIGS) + len(I.VARIANTS)
+
+
+def test_pooled_positions_are_cell_means():
+    """A pooled tier's positions are the mean of the full-resolution positions
+    each cell covers (the cell centre), as the oracle pools them."""
+    from oracle import pool64
+    for s in (2, 4):
+        full = I.frame_positions([1, 2], 48, 84)
+        pooled = I.frame_positions([1, 2], 48, 84, pool=s)
+        np.testing.assert_array_equal(pooled, pool64.pool_frames(full[:, None, :], 48, 84, s)[:, 0, :])
