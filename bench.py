@@ -165,9 +165,11 @@ def _time(fn, stream, steps):
 
 
 def other_workloads(steps, skip):
-    """Forward time of the other 1344x768 workloads (hierarchical history,
-    joint video+audio, and the query-side variants: history + current as
-    queries, the 7-frame first window, the prefix self-attention pass), and
+    """Forward and per-chunk pack time of the other 1344x768 workloads
+    (hierarchical history, with its pooled tiers given or produced by the pack
+    from full-resolution frames; joint video+audio; the query-side variants:
+    history + current as queries, the 7-frame first window, the prefix
+    self-attention pass), and
     the 40 audio-only queries of the video+audio chunk run over 32 key splits
     + merge vs one plain forward. Extra lines, not the metric."""
     import torch
@@ -177,14 +179,15 @@ def other_workloads(steps, skip):
     stream = torch.cuda.current_stream()
     res = {}
     makers = [f for n, f in list(I.CONFIGS.items()) + list(I.VARIANTS.items())
-              if n != skip and f().nq >= 4096]
+              if n != skip and f().nq >= 4096] + [I.hier_pooled_1344x768]
     for make in makers:
         w = make()
         ca = ChunkAttention(w, device="cuda:0")
         ca.pack_static(stream)
         ca.step(stream)
         ms = _time(lambda: ca.forward(stream), stream, steps)
-        res[w.name] = {"nq": w.nq, "nk": w.nk, "forward_ms": ms,
+        pack = _time(lambda: (ca._tables(True, stream), ca._pack(True, stream)), stream, steps)
+        res[w.name] = {"nq": w.nq, "nk": w.nk, "forward_ms": ms, "pack_tables_ms": pack,
                        "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12}
         if w.name == "video_audio_1344x768":
             q, qt = ca.q[w.nq - 40:], ca.q_table[w.nq - 40:]

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 /* Packed context capacity (rows) must be a multiple of this (one key tile). */
 #define SA_ROW_ALIGN 64
@@ -59,6 +59,8 @@ extern "C" {
 #define SA_MAX_SEGMENTS 16
 /* Most key splits of sa_forward_split / sa_combine_splits. */
 #define SA_MAX_SPLITS 256
+/* Largest spatial pooling factor of a segment (sa_segment.pool). */
+#define SA_MAX_POOL 8
 
 typedef int32_t sa_status;
 #define SA_OK 0
@@ -145,7 +147,31 @@ typedef struct {
     int64_t dst_row;       /* first packed row this segment fills */
     const sa_rmsnorm *k_norm; /* host pointer, or NULL: keys taken as given. When set, every key
                                  row is RMS-normalised (before its rotation, if any) */
+    int32_t pool;          /* 0 or 1: k, v hold the segment's rows as they are packed.
+                              2..SA_MAX_POOL: k, v hold full-resolution latent frames and the
+                              pack writes their pool x pool spatial means (a coarser history
+                              tier, see below) */
+    int32_t pool_grid_h;   /* pool > 1: token grid of one full-resolution frame, rows */
+    int32_t pool_grid_w;   /* pool > 1: token grid of one full-resolution frame, columns */
 } sa_segment;
+
+/*
+ * Pooled segments (pool = s > 1): older history is kept at progressively
+ * lower spatial resolution (AlayaRenderer-Flash page, key contributions and
+ * technical details); the pages fix neither the operator nor its place, and
+ * the reading implemented is the spatial mean of the keys before their
+ * normalisation and rotation, and of the values. k and v then hold
+ * F = rows / ((pool_grid_h / s) (pool_grid_w / s)) frames of
+ * pool_grid_h x pool_grid_w tokens, full-resolution row (f, y, x) at index
+ * (f pool_grid_h + y) pool_grid_w + x (strides as above). Packed row
+ * dst_row + (f (pool_grid_h / s) + i) (pool_grid_w / s) + j receives the mean
+ * of rows (f, s i + a, s j + b), a, b in [0, s), summed in float32 and scaled
+ * by 1/s^2; its key is then normalised (k_norm) and rotated by entry
+ * (f, i, j) of rope -- one entry per pooled row, normally the cell centre
+ * (s i + (s-1)/2, s j + (s-1)/2) -- and rounded once, like any other key.
+ * pool_grid_h and pool_grid_w must be positive multiples of s and rows a
+ * multiple of (pool_grid_h / s)(pool_grid_w / s). The time axis is not pooled.
+ */
 
 /*
  * A packed key/value context: the persistent per-layer buffers the forward
@@ -192,7 +218,8 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
  * Each segment's rows are written to packed rows [dst_row, dst_row + rows),
  * keys RMS-normalised when the segment has a k_norm and rotated by the
  * segment's table (both fused into the load: no separate pass), values copied
- * (bf16: transposed as documented above). A call that
+ * (bf16: transposed as documented above); a pooled segment's rows are first
+ * formed as the spatial means of its full-resolution frames, in the same load. A call that
  * packs at least one row also writes zeros to the padding rows [ctx->rows,
  * next multiple of SA_ROW_ALIGN) of every head. Other packed rows not covered
  * by a segment of this call are left untouched, so the static prefix (prompt,
@@ -200,7 +227,7 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
  * current chunk) rewritten in place every chunk.
  * Segment row ranges must lie inside [0, ctx->rows) and must not overlap.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE (n_segs outside [0, SA_MAX_SEGMENTS],
- * ranges, strides), SA_ERR_CAPACITY, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
+ * ranges, strides, pooling factor or grid), SA_ERR_CAPACITY, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
  * SA_ERR_ALIGN, SA_ERR_HIP.
  */
 sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t n_segs, hipStream_t stream);

@@ -46,7 +46,8 @@ class Segment(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("k_row_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
                 ("v_row_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
-                ("rope", ctypes.c_void_p), ("dst_row", ctypes.c_int64), ("k_norm", ctypes.c_void_p)]
+                ("rope", ctypes.c_void_p), ("dst_row", ctypes.c_int64), ("k_norm", ctypes.c_void_p),
+                ("pool", ctypes.c_int32), ("pool_grid_h", ctypes.c_int32), ("pool_grid_w", ctypes.c_int32)]
 
 
 class Norm:
@@ -182,31 +183,42 @@ class PackedContext:
                        self.k_packed.data_ptr(), self.v_packed.data_ptr())
 
 
-def make_segment(k, v, dst_row, rope=None, k_norm=None):
+def make_segment(k, v, dst_row, rope=None, k_norm=None, pool=None):
     """C segment descriptor for K/V views [rows][heads][head_dim] starting at
     packed row dst_row. ``k_norm`` is a ctypes RmsNorm the caller keeps alive
-    for the call, or None."""
+    for the call, or None. ``pool`` = ``(s, grid_h, grid_w)``: k and v hold
+    whole full-resolution frames of grid_h x grid_w tokens and the segment
+    packs their s x s spatial means (rows = frames * (grid_h/s) * (grid_w/s))."""
     krs, khs = _rows_heads(k, "k")
     vrs, vhs = _rows_heads(v, "v")
     if k.shape[0] != v.shape[0]:
         raise ValueError("k and v must have the same number of rows")
-    return Segment(k.data_ptr(), v.data_ptr(), k.shape[0], krs, khs, vrs, vhs,
+    rows = k.shape[0]
+    s = gh = gw = 0
+    if pool is not None:
+        s, gh, gw = (int(x) for x in pool)
+        if s < 1 or gh < 1 or gw < 1 or gh % s or gw % s or rows % (gh * gw):
+            raise ValueError(f"pooling {pool} does not cut {rows} rows into whole frames of whole cells")
+        rows = rows // (gh * gw) * (gh // s) * (gw // s)
+    return Segment(k.data_ptr(), v.data_ptr(), rows, krs, khs, vrs, vhs,
                    None if rope is None else rope.data_ptr(), dst_row,
-                   None if k_norm is None else ctypes.cast(ctypes.pointer(k_norm), ctypes.c_void_p))
+                   None if k_norm is None else ctypes.cast(ctypes.pointer(k_norm), ctypes.c_void_p), s, gh, gw)
 
 
 def sa_pack_context(ctx, segments, stream=None, k_norm=None):
-    """Pack ``segments`` (list of (k, v, dst_row, rope_or_None[, norm_or_None]))
-    into ``ctx``. A segment's own norm (a ``Norm``) wins over ``k_norm``, the
-    default for every segment."""
+    """Pack ``segments`` (list of (k, v, dst_row, rope_or_None[, norm_or_None
+    [, pool_or_None]])) into ``ctx``. A segment's own norm (a ``Norm``) wins
+    over ``k_norm``, the default for every segment; ``pool`` is
+    ``(s, grid_h, grid_w)`` as in :func:`make_segment`."""
     keep = []
     segs = []
     for seg in segments:
         k, v, dst, rope = seg[:4]
         norm = seg[4] if len(seg) > 4 else k_norm
+        pool = seg[5] if len(seg) > 5 else None
         n = None if norm is None else norm.struct()
         keep.append(n)
-        segs.append(make_segment(k, v, dst, rope, n))
+        segs.append(make_segment(k, v, dst, rope, n, pool))
     arr = (Segment * max(1, len(segs)))(*segs)
     c = ctx.struct()
     _check("sa_pack_context", lib().sa_pack_context(ctypes.byref(c), arr, len(segs), _stream(stream)))

@@ -196,8 +196,23 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
         snprintf(what, sizeof what, "segment %d: k_norm", i);
         st = check_norm(s.k_norm, what, kn);
         if (st != SA_OK) return st;
+        if (s.pool < 0 || s.pool > SA_MAX_POOL)
+            return fail(SA_ERR_SHAPE, "segment %d: pool %d outside [0, %d]", i, s.pool, SA_MAX_POOL);
+        const int32_t pool = s.pool > 1 ? s.pool : 1;
+        if (pool > 1) {
+            if (s.pool_grid_h <= 0 || s.pool_grid_w <= 0 || s.pool_grid_h % pool || s.pool_grid_w % pool)
+                return fail(SA_ERR_SHAPE, "segment %d: pooling grid %d x %d is not made of whole %d x %d cells", i,
+                            s.pool_grid_h, s.pool_grid_w, pool, pool);
+            const int64_t cells = (int64_t)(s.pool_grid_h / pool) * (s.pool_grid_w / pool);
+            if (s.rows % cells)
+                return fail(SA_ERR_SHAPE, "segment %d: rows %lld is not a whole number of pooled frames (%lld rows)",
+                            i, (long long)s.rows, (long long)cells);
+        }
         sa::PackSeg &p = a.seg[used++];
         p.norm = kn;
+        p.pool = pool;
+        p.grid_h = pool > 1 ? s.pool_grid_h : 0;
+        p.grid_w = pool > 1 ? s.pool_grid_w : 0;
         p.k = s.k;
         p.v = s.v;
         p.rope = s.rope;

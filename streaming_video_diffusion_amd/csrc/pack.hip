@@ -5,6 +5,9 @@
 // inference-acceleration section), and fuse rotary encoding with the cache
 // write (same page, Fast Causal H3 VAE section). Here one workgroup owns one
 // 64-row tile of the packed row space for one head and one segment:
+//   * pooled segments (older history at coarser resolution, AlayaRenderer-Flash
+//     page, key contributions): each packed row first forms the s x s spatial
+//     mean of its full-resolution source rows, for keys and values alike;
 //   * keys: 16-byte coalesced loads, optional RMS normalisation (QK-norm) and
 //     rotation in float32 by the segment's table, one rounding to bfloat16,
 //     16-byte stores into K [H][C][d];
@@ -44,6 +47,43 @@ __device__ __forceinline__ void norm_row(float (&x)[E], const NormArgs &n, int h
     const float *w = n.weight ? n.weight + (n.per_head ? (int64_t)h * d : 0) + c0 : nullptr;
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = x[e] * r * (w ? w[e] : 1.0f);
+}
+
+// Spatial mean behind pooled row sr of a pooled segment (pool = P > 1): the
+// row is cell (i, j) of frame f on the (grid_h/P) x (grid_w/P) pooled grid and
+// averages the P x P full-resolution rows (f, P i + a, P j + b). One 16-byte
+// chunk (E elements) of K and of V, at element offsets koff / voff within a
+// row, is summed in float32 and scaled by 1/P^2.
+template <typename VT, int E, typename T>
+__device__ __forceinline__ void pooled_chunk(const PackSeg &s, const T *ks, const T *vs, int64_t sr, int64_t koff,
+                                             int64_t voff, float (&kx)[E], float (&vx)[E]) {
+    const int P = s.pool;
+    const int pw = s.grid_w / P;
+    const int64_t cells = (int64_t)(s.grid_h / P) * pw;
+    const int64_t f = sr / cells;
+    const int c = (int)(sr - f * cells);
+    const int i = c / pw, j = c - i * pw;
+    const int64_t base = (f * s.grid_h + (int64_t)P * i) * s.grid_w + (int64_t)P * j;
+#pragma unroll
+    for (int e = 0; e < E; ++e) kx[e] = vx[e] = 0.f;
+    for (int a = 0; a < P; ++a) {
+        for (int b = 0; b < P; ++b) {
+            const int64_t r = base + (int64_t)a * s.grid_w + b;
+            const VT kr = *reinterpret_cast<const VT *>(ks + r * s.k_rs + koff);
+            const VT vr = *reinterpret_cast<const VT *>(vs + r * s.v_rs + voff);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                kx[e] += (float)kr[e];
+                vx[e] += (float)vr[e];
+            }
+        }
+    }
+    const float inv = 1.0f / (float)(P * P);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kx[e] *= inv;
+        vx[e] *= inv;
+    }
 }
 
 struct TileRange {
@@ -87,10 +127,19 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
         const int64_t row = r.tile_start + lr;
         if (row < r.lo || row >= r.hi) continue;
         const int64_t sr = row - s.dst_row;
-        const bf16x8 kraw = *reinterpret_cast<const bf16x8 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 8);
         float x[8];
+        bf16x8 vv;
+        if (s.pool > 1) {
+            float vx[8];
+            pooled_chunk<bf16x8, 8>(s, ks, vs, sr, h * s.k_hs + chunk * 8, h * s.v_hs + chunk * 8, x, vx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)kraw[e];
+            for (int e = 0; e < 8; ++e) vv[e] = (bf16)vx[e];
+        } else {
+            const bf16x8 kraw = *reinterpret_cast<const bf16x8 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)kraw[e];
+            vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
+        }
         if (s.norm.on) norm_row<CH, 8>(x, s.norm, h, D, chunk * 8);
         if (s.rope) {
             const f32x4 *tb = reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 4) * 2);
@@ -108,7 +157,6 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kv[e] = (bf16)x[e];
         *reinterpret_cast<bf16x8 *>(kp + row * D + chunk * 8) = kv;
-        const bf16x8 vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
         *reinterpret_cast<bf16x8 *>(sv + lr * PITCH + chunk * 8) = vv;
     }
     __syncthreads();
@@ -165,7 +213,16 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
         const int64_t row = r.tile_start + t / CH + p * RPP;
         if (row < r.lo || row >= r.hi) continue;
         const int64_t sr = row - s.dst_row;
-        f32x4 kv = *reinterpret_cast<const f32x4 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 4);
+        f32x4 kv, vv;
+        if (s.pool > 1) {
+            float kx[4], vx[4];
+            pooled_chunk<f32x4, 4>(s, ks, vs, sr, h * s.k_hs + chunk * 4, h * s.v_hs + chunk * 4, kx, vx);
+            kv = f32x4{kx[0], kx[1], kx[2], kx[3]};
+            vv = f32x4{vx[0], vx[1], vx[2], vx[3]};
+        } else {
+            kv = *reinterpret_cast<const f32x4 *>(ks + sr * s.k_rs + h * s.k_hs + chunk * 4);
+            vv = *reinterpret_cast<const f32x4 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 4);
+        }
         if (s.norm.on) {
             float x[4] = {kv.x, kv.y, kv.z, kv.w};
             norm_row<CH, 4>(x, s.norm, h, D, chunk * 4);
@@ -180,8 +237,7 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
             kv.w = x.z * cs.w + x.w * cs.z;
         }
         *reinterpret_cast<f32x4 *>(kp + row * D + chunk * 4) = kv;
-        *reinterpret_cast<f32x4 *>(vp + row * D + chunk * 4) =
-            *reinterpret_cast<const f32x4 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 4);
+        *reinterpret_cast<f32x4 *>(vp + row * D + chunk * 4) = vv;
     }
 }
 

@@ -46,6 +46,8 @@ struct PackSeg {
     const float *rope;
     int64_t rows, k_rs, k_hs, v_rs, v_hs, dst_row;
     NormArgs norm;
+    int32_t pool;            // 1: rows as given; s > 1: s x s spatial means of full-resolution frames
+    int32_t grid_h, grid_w;  // full-resolution frame grid (pool > 1)
 };
 struct PackArgs {
     void *k_packed;

@@ -93,6 +93,13 @@ class Segment:
     rows: int
     pos: object          # float32 [rows][3] or None (no rotary encoding)
     dynamic: bool        # re-packed every chunk (False: persistent prefix)
+    pool: int = 1        # > 1: rows are s x s spatial means the pack forms from full-resolution frames
+    grid: tuple = None   # (grid_h, grid_w) of those full-resolution frames
+
+    @property
+    def src_rows(self):
+        """Rows of the segment's source tensors (full resolution when pooled)."""
+        return self.rows * self.pool * self.pool
 
 
 @dataclass
@@ -146,8 +153,9 @@ class Workload:
         return self._draw(call, 0, self.nq)
 
     def kv(self, seg, call=0):
-        """Keys and values of segment index ``seg`` for call ``call``."""
-        rows = self.segments[seg].rows
+        """Keys and values of segment index ``seg`` for call ``call`` (the
+        full-resolution frames of a pooled segment)."""
+        rows = self.segments[seg].src_rows
         return self._draw(call, 1 + 2 * seg, rows), self._draw(call, 2 + 2 * seg, rows)
 
     def norm_weights(self):
@@ -163,15 +171,20 @@ class Workload:
         return tuple(out)
 
 
-def _video_segments(prompt, grid_h, grid_w, ref_t, tiers, cur_t, audio=0):
-    """Build segments: prompt, ref, history tiers (oldest first), current."""
+def _video_segments(prompt, grid_h, grid_w, ref_t, tiers, cur_t, audio=0, produce=False):
+    """Build segments: prompt, ref, history tiers (oldest first), current.
+    ``produce``: pooled tiers are formed by the pack from full-resolution
+    frames (else they are given at their pooled size)."""
     segs = [Segment("prompt", prompt, None, False),
             Segment("ref", grid_h * grid_w, frame_positions([ref_t], grid_h, grid_w), False)]
     for name, t_values, pool in tiers:
         pos = frame_positions(t_values, grid_h, grid_w, pool)
         if audio and pool == 1:
             pos = np.concatenate([pos, audio_positions(t_values[0], audio)])
-        segs.append(Segment(name, int(pos.shape[0]), pos, True))
+        if produce and pool > 1:
+            segs.append(Segment(name, int(pos.shape[0]), pos, True, pool=pool, grid=(grid_h, grid_w)))
+        else:
+            segs.append(Segment(name, int(pos.shape[0]), pos, True))
     cur = frame_positions(cur_t, grid_h, grid_w)
     if audio:
         cur = np.concatenate([cur, audio_positions(cur_t[0], audio)])
@@ -206,6 +219,23 @@ def hier_1344x768():
     segs, cur = _video_segments(256, 48, 84, 0, tiers, [10, 11, 12])
     return Workload("hier_1344x768", 4, "bf16", 40, 128, cur, segs,
                     description="1344x768 hierarchical history: 12096 q x 32260 kv, 40 heads, d128")
+
+
+def hier_pooled(name, cfg_id, dtype, heads, head_dim, grid_h, grid_w, prompt, qk_norm=None):
+    """Hierarchical history whose pooled tiers the pack produces from
+    full-resolution frames: 4x4 tier of frames 1-3, 2x2 tier of frames 4-6,
+    full-resolution previous chunk 7-9, current chunk 10-12."""
+    tiers = [("pool4", [1, 2, 3], 4), ("pool2", [4, 5, 6], 2), ("prev", [7, 8, 9], 1)]
+    segs, cur = _video_segments(prompt, grid_h, grid_w, 0, tiers, [10, 11, 12], produce=True)
+    return Workload(name, cfg_id, dtype, heads, head_dim, cur, segs, qk_norm=qk_norm,
+                    description=f"hierarchical history, pooled tiers produced from full resolution: "
+                                f"{3 * grid_h * grid_w} q, {heads} heads, d{head_dim}")
+
+
+def hier_pooled_1344x768():
+    """The hierarchical 1344x768 context with its 4x4 and 2x2 tiers pooled by
+    the pack from full-resolution frames (same attention shape: 12096 q x 32260 kv)."""
+    return hier_pooled("hier_pooled_1344x768", 9, "bf16", 40, 128, 48, 84, 256)
 
 
 def video_audio_1344x768():

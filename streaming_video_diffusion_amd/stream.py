@@ -56,8 +56,9 @@ class ChunkAttention:
             if s.pos is not None and not shares_q and s.rows > 0:
                 pos = torch.from_numpy(s.pos).to(dev)
                 table = torch.empty((s.rows, w.head_dim // 2, 2), dtype=torch.float32, device=dev)
+            pool = (s.pool, s.grid[0], s.grid[1]) if s.pool > 1 else None
             self.segs.append(dict(name=s.name, k=up(k), v=up(v), pos=pos, table=table, dst=row,
-                                  dynamic=s.dynamic, rotary=s.pos is not None, shares_q=shares_q))
+                                  dynamic=s.dynamic, rotary=s.pos is not None, shares_q=shares_q, pool=pool))
             row += s.rows
         self.q_norm = self.k_norm = None
         weights = w.norm_weights()
@@ -82,8 +83,8 @@ class ChunkAttention:
             if s["dynamic"] != dynamic:
                 continue
             rope = self.q_table if s["shares_q"] else (s["table"] if s["rotary"] else None)
-            segs.append((s["k"], s["v"], s["dst"], rope))
-        B.sa_pack_context(self.ctx, segs, stream=stream, k_norm=self.k_norm)
+            segs.append((s["k"], s["v"], s["dst"], rope, self.k_norm, s["pool"]))
+        B.sa_pack_context(self.ctx, segs, stream=stream)
 
     def pack_static(self, stream=None):
         """Build the static prefix's tables and pack it (once per bank)."""
@@ -102,12 +103,14 @@ class ChunkAttention:
         return self.out
 
     def host_inputs(self):
-        """The exact host values fed to the device (for the oracle)."""
+        """The exact host values fed to the device (for the oracle): queries,
+        query positions and ``(k, v, pos)`` per segment; a pooled segment gives
+        its full-resolution frames as ``(k, v, pos, (grid_h, grid_w, s))``."""
         w = self.w
         segs = []
         for i, s in enumerate(w.segments):
             k, v = w.kv(i, self.call)
-            segs.append((k, v, s.pos))
+            segs.append((k, v, s.pos, (s.grid[0], s.grid[1], s.pool)) if s.pool > 1 else (k, v, s.pos))
         return w.q(self.call), w.q_pos, segs
 
     def host_norms(self):

@@ -6,7 +6,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle import attn64
+from oracle import attn64, pool64
 from streaming_video_diffusion_amd.stream import ChunkAttention
 
 # Parity bounds against the fp64 oracle.
@@ -64,8 +64,21 @@ def run(workload, call=0, out_dtype=None):
     return ca, out.float().cpu().numpy().astype(np.float64)
 
 
+def attention_segments(segs):
+    """Segments as attention sees them: a pooled segment's full-resolution
+    frames pooled by the oracle."""
+    out = []
+    for seg in segs:
+        if len(seg) == 4:
+            k, v, pos, (gh, gw, s) = seg
+            seg = (pool64.pool_frames(k, gh, gw, s), pool64.pool_frames(v, gh, gw, s), pos)
+        out.append(seg)
+    return out
+
+
 def oracle(ca, rows=None):
     q, q_pos, segs = ca.host_inputs()
     qn, kn = ca.host_norms()
     w = ca.w
-    return attn64.chunk_attention(q, q_pos, segs, w.axis_dims, w.theta, w.scale, rows=rows, q_norm=qn, k_norm=kn)
+    return attn64.chunk_attention(q, q_pos, attention_segments(segs), w.axis_dims, w.theta, w.scale, rows=rows,
+                                  q_norm=qn, k_norm=kn)

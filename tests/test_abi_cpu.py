@@ -47,14 +47,15 @@ def test_header_constants_match_binding():
     for name, val in ERR.items():
         assert re.search(rf"#define SA_ERR_{name} \({val}\)", text), name
     assert ctypes.sizeof(B.RopeSpec) == 24
-    assert ctypes.sizeof(B.Segment) == 80
+    assert ctypes.sizeof(B.Segment) == 96
     assert ctypes.sizeof(B.Context) == 48
     assert ctypes.sizeof(B.RmsNorm) == 16
-    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 2
+    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 3
+    assert int(re.search(r"#define SA_MAX_POOL (\d+)", text).group(1)) == 8
 
 
 def test_version_and_status_strings(L):
-    assert L.sa_abi_version() == 2
+    assert L.sa_abi_version() == 3
     assert L.sa_status_string(0) == b"SA_OK"
     for name, val in ERR.items():
         assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
@@ -122,11 +123,11 @@ def norm(weight=None, eps=1e-6, per_head=0):
 
 def seg(**kw):
     s = dict(k=FAKE, v=FAKE, rows=16, k_row_stride=256, k_head_stride=128, v_row_stride=256, v_head_stride=128,
-             rope=None, dst_row=0, k_norm=None)
+             rope=None, dst_row=0, k_norm=None, pool=0, gh=0, gw=0)
     s.update(kw)
     kn = None if s["k_norm"] is None else ctypes.cast(ctypes.pointer(s["k_norm"]), ctypes.c_void_p)
     return B.Segment(s["k"], s["v"], s["rows"], s["k_row_stride"], s["k_head_stride"], s["v_row_stride"],
-                     s["v_head_stride"], s["rope"], s["dst_row"], kn)
+                     s["v_head_stride"], s["rope"], s["dst_row"], kn, s["pool"], s["gh"], s["gw"])
 
 
 @pytest.mark.parametrize("c,segs,err", [
@@ -152,6 +153,11 @@ def seg(**kw):
     (ctx(), [seg(k_norm=norm(eps=float("nan")))], "SHAPE"),
     (ctx(), [seg(k_norm=norm(per_head=2))], "SHAPE"),
     (ctx(), [seg(k_norm=norm(weight=FAKE + 4))], "ALIGN"),
+    (ctx(), [seg(pool=-1)], "SHAPE"),
+    (ctx(), [seg(pool=9, gh=9, gw=9)], "SHAPE"),
+    (ctx(), [seg(pool=2, gh=0, gw=8)], "SHAPE"),
+    (ctx(), [seg(pool=2, gh=6, gw=7)], "SHAPE"),
+    (ctx(), [seg(pool=4, gh=8, gw=16, rows=12)], "SHAPE"),  # 8 pooled cells a frame: 12 rows is no whole frame
 ])
 def test_pack_errors(L, c, segs, err):
     arr = (B.Segment * len(segs))(*segs)
