@@ -197,7 +197,7 @@ typedef struct {
     int32_t head_dim;      /* 64 or 128 */
     sa_dtype dtype;        /* element type of K, V (and of Q in sa_forward) */
     int64_t capacity_rows; /* allocated rows, a multiple of SA_ROW_ALIGN; one head's packed
-                              K (or V), capacity_rows * head_dim * element size, at most 2^31 bytes */
+                              K (or V), capacity_rows * head_dim * element size, below 2^31 bytes */
     int64_t rows;          /* valid rows Nk, 1 <= rows <= capacity_rows for sa_forward */
     void *k_packed;        /* device, sa_packed_bytes() bytes */
     void *v_packed;        /* device, sa_packed_bytes() bytes */
@@ -207,7 +207,7 @@ typedef struct {
  * sa_packed_bytes -- size in bytes of each of k_packed and v_packed.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
  * SA_ERR_CAPACITY (capacity_rows not a multiple of SA_ROW_ALIGN, or one head's
- * packed K/V above 2^31 bytes).
+ * packed K/V not below 2^31 bytes).
  */
 sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64_t capacity_rows,
                           size_t *bytes_each);

@@ -48,8 +48,8 @@ sa_status check_context(const sa_context *ctx) {
         return fail(SA_ERR_CAPACITY, "ctx->capacity_rows %lld is not a non-negative multiple of %d",
                     (long long)ctx->capacity_rows, SA_ROW_ALIGN);
     // one head's packed K (or V) must stay below 2^31 bytes (32-bit in-head offsets)
-    if (ctx->capacity_rows * ctx->head_dim * elem_bytes(ctx->dtype) > (int64_t(1) << 31))
-        return fail(SA_ERR_CAPACITY, "ctx->capacity_rows %lld: one head's packed K/V above 2^31 bytes",
+    if (ctx->capacity_rows * ctx->head_dim * elem_bytes(ctx->dtype) >= (int64_t(1) << 31))
+        return fail(SA_ERR_CAPACITY, "ctx->capacity_rows %lld: one head's packed K/V not below 2^31 bytes",
                     (long long)ctx->capacity_rows);
     if (ctx->rows < 0 || ctx->rows > ctx->capacity_rows)
         return fail(SA_ERR_CAPACITY, "ctx->rows %lld outside [0, capacity_rows %lld]", (long long)ctx->rows,
@@ -144,9 +144,9 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
     if (heads < 1 || heads > 65535) return fail(SA_ERR_SHAPE, "heads %d outside [1, 65535]", heads);
     if (!supported_dim(head_dim)) return fail(SA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (capacity_rows < 0 || capacity_rows % SA_ROW_ALIGN != 0 ||
-        capacity_rows * head_dim * elem_bytes(dtype) > (int64_t(1) << 31))
+        capacity_rows * head_dim * elem_bytes(dtype) >= (int64_t(1) << 31))
         return fail(SA_ERR_CAPACITY,
-                    "capacity_rows %lld is not a multiple of %d with one head's K/V at most 2^31 bytes",
+                    "capacity_rows %lld is not a multiple of %d with one head's K/V below 2^31 bytes",
                     (long long)capacity_rows, SA_ROW_ALIGN);
     *bytes_each = (size_t)heads * (size_t)capacity_rows * (size_t)head_dim * (size_t)elem_bytes(dtype);
     return SA_OK;

@@ -51,6 +51,12 @@ constexpr int BN = 64;                // keys per tile
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// 16-byte operand read at an LDS byte address.
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+    return *reinterpret_cast<lds_bf16x8 *>((uintptr_t)addr);
+}
 
 // Physical 16-byte chunk of a tile row: XOR swizzles that keep the matrix-core
 // operand reads (32 rows, one logical chunk) free of LDS bank conflicts for
@@ -119,23 +125,25 @@ struct Tile {
         return pl;
     }
 
-    // Issue this wave's share of the direct global->LDS loads of one K/V^T
-    // tile: a wave-uniform tile base plus the loop-invariant lane offsets. The
-    // packed capacity is a multiple of the tile, so the last tile never leaves
-    // the allocation; its rows past nk hold zeros written by the pack step,
-    // and their scores are masked.
-    __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, const unsigned char *kb,
-                                                 const unsigned char *vb, int64_t k0, int w) {
-        const unsigned char *kt = kb + k0 * KROW;
-        const unsigned char *vt = vb + k0 * 2;
+    // Issue this wave's share of the direct buffer->LDS loads of one K/V^T
+    // tile: the loop-invariant lane offsets plus the tile's wave-uniform byte
+    // offset (a scalar operand). kr / vr describe one head's packed K / V^T
+    // (below 2^31 bytes each). The packed capacity is a multiple of the tile,
+    // so the last tile never leaves the allocation; its rows past nk hold
+    // zeros written by the pack step, and their scores are masked. (Buffer
+    // rather than global loads: with a global load to LDS in flight the
+    // compiler can only wait for all LDS reads at once, which would undo the
+    // read-ahead of the operand reads.)
+    __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, __amdgpu_buffer_rsrc_t kr,
+                                                 __amdgpu_buffer_rsrc_t vr, uint32_t k0, int w) {
 #pragma unroll
         for (int ii = 0; ii < KINSTR / NW; ++ii)
-            __builtin_amdgcn_global_load_lds(kt + pl.k[ii], (lds_void *)(buf + (w * (KINSTR / NW) + ii) * 1024), 16,
-                                             0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(buf + (w * (KINSTR / NW) + ii) * 1024), 16,
+                                                     (int)pl.k[ii], (int)(k0 * KROW), 0, 0);
 #pragma unroll
         for (int ii = 0; ii < VINSTR / NW; ++ii)
-            __builtin_amdgcn_global_load_lds(vt + pl.v[ii],
-                                             (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024),
+                                                     16, (int)pl.v[ii], (int)(k0 * 2), 0, 0);
     }
 
 };
@@ -243,8 +251,15 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int c = 0; c < DT; ++c) o[c] = f32x16{};
     float l = 0.f;
 
-    const unsigned char *kb = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)head * a.cap * D * 2;
-    const unsigned char *vb = reinterpret_cast<const unsigned char *>(a.v) + (int64_t)head * D * a.cap * 2;
+    // Buffer descriptors of this head's packed K and V^T (raw, byte-addressed,
+    // 32-bit data format word as the CDNA buffer instructions expect).
+    const int head_bytes = (int)(a.cap * D * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<unsigned char *>(const_cast<void *>(a.k)) + (int64_t)head * a.cap * D * 2, 0, head_bytes,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<unsigned char *>(const_cast<void *>(a.v)) + (int64_t)head * D * a.cap * 2, 0, head_bytes,
+        0x00020000);
     const int ntiles_all = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
     // This workgroup's key tiles [t_begin, ntiles) (all of them without split-KV).
@@ -252,8 +267,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int ntiles = split_first_tile(split + 1, a.n_splits, ntiles_all);
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     const f32x16 zero16 = f32x16{};
-    const uint32_t A0 = T::kbase(l32, hf);
-    const uint32_t B0 = T::vbase(l32, hf);
+    // Per-lane operand-read bases as LDS byte addresses. smem is 1024-byte
+    // aligned and every buffer starts at a multiple of 32 KiB, so the XOR
+    // swizzle (bits 5..7) commutes with adding either.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
+    const uint32_t A0 = T::kbase(l32, hf) + lds0;
+    const uint32_t B0 = T::vbase(l32, hf) + lds0;
 
     // Every tile follows one schedule on every path: at tile kt a wave issues
     // its share of tile kt+2's direct loads, computes, waits for its own loads
@@ -265,7 +284,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     // the lane id: a few VALU ops instead of per-lane 64-bit pointers kept
     // live across the loop, and the loads keep the SGPR-base form.
     auto issue = [&](int kt) __attribute__((always_inline)) {
-        if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), kb, vb, (int64_t)kt * BN, wu);
+        if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), krs, vrs, (uint32_t)(kt * BN), wu);
     };
     auto end_tile = [&]() __attribute__((always_inline)) {
         vmcnt0();
@@ -276,7 +295,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     auto qk = [&](const unsigned char *buf, f32x16 (&s)[2], const f32x16 &seed) __attribute__((always_inline)) {
         const uint32_t kb0 = (uint32_t)(buf - smem) + A0;
         auto kread = [&](int j, int tt) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8 *>(smem + ((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW));
+            return lds_read16((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW);
         };
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
@@ -312,7 +331,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     auto exp_pv = [&](const unsigned char *buf, const f32x16 (&s)[2], const float m) __attribute__((always_inline)) {
         const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
         auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8 *>(smem + ((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW));
+            return lds_read16((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW);
         };
         float ls[2] = {0.f, 0.f};
 #pragma unroll
@@ -349,10 +368,10 @@ void fwd_bf16_kernel(FwdArgs a) {
         const uint32_t kb0 = (uint32_t)(nbuf - smem) + A0;
         const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
         auto kread = [&](int j, int tt) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8 *>(smem + ((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW));
+            return lds_read16((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW);
         };
         auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8 *>(smem + ((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW));
+            return lds_read16((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW);
         };
         constexpr int KSTEPS_PER_GROUP = DC / 4;
         bf16x8 kr[DC][2];
@@ -456,22 +475,27 @@ void fwd_bf16_kernel(FwdArgs a) {
     issue(t_begin);
     issue(t_begin + 1);
     end_tile();
-    f32x16 s[2];
+    // Two score sets alternate roles (unrolled by two), so no copy of the
+    // next tile's scores is needed between tiles.
+    f32x16 s[2], sb[2];
     qk(buf_of(t_begin), s, zero16);
-    for (int kt = t_begin; kt < ntiles; ++kt) {
-        // On the last tile the next-tile scores read a resident buffer and are
+    int kt = t_begin;
+    for (; kt + 1 < ntiles; kt += 2) {
+        issue(kt + 2);
+        mask(s, kt);
+        qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
+        end_tile();
+        issue(kt + 3);
+        mask(sb, kt + 1);
+        qk_exp_pv(buf_of(kt + 2), s, buf_of(kt + 1), sb);
+        end_tile();
+    }
+    if (kt < ntiles) {
+        // Last (odd) tile: the next-tile scores read a resident buffer and are
         // discarded.
         issue(kt + 2);
         mask(s, kt);
-        f32x16 sn[2];
-#if SA_FWD_HAND
-        qk_exp_pv(buf_of(kt + 1), sn, buf_of(kt), s);
-#else
-        qk(buf_of(kt + 1), sn, zero16);
-        exp_pv(buf_of(kt), s, 0.0f);
-#endif
-        s[0] = sn[0];
-        s[1] = sn[1];
+        qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
         end_tile();
     }
 
@@ -495,10 +519,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     // subtracted in the exponent; m is raised when a tile's max exceeds it by
     // more than 2^8, and O and l are rescaled on every tile (by exactly 1 when
     // m does not move).
-    // Workgroup vote through LDS: one flag per wave in the third buffer, which
-    // the second pass's first two tile loads do not touch (every wave reads
-    // the flags before the barrier that follows those loads).
-    unsigned *flags = reinterpret_cast<unsigned *>(smem + 2 * T::BUF);
+    // Workgroup vote through LDS: one flag per wave in the buffer of tile
+    // t_begin + 2, which the second pass's first two tile loads (tiles t_begin
+    // and t_begin + 1) do not touch; every wave reads the flags before the
+    // barrier that follows those loads, and only after it is that buffer
+    // loaded again.
+    unsigned *flags = reinterpret_cast<unsigned *>(buf_of(t_begin + 2));
     const unsigned wave_fail = __any(row && !ok) ? 1u : 0u;  // vote of the whole wave, outside the lane-0 branch
     if (lane == 0) flags[w] = wave_fail;
     __syncthreads();

@@ -103,6 +103,10 @@ def test_packed_bytes(L):
     assert L.sa_packed_bytes(0, 128, B.SA_BF16, 32, ctypes.byref(n)) == ERR["SHAPE"]
     assert L.sa_packed_bytes(4, 128, 7, 32, ctypes.byref(n)) == ERR["DTYPE"]
     assert L.sa_packed_bytes(4, 128, B.SA_BF16, 32, None) == ERR["NULL"]
+    # one head's packed K/V must stay below 2^31 bytes (32-bit in-head offsets)
+    assert L.sa_packed_bytes(1, 128, B.SA_BF16, 8388608, ctypes.byref(n)) == ERR["CAPACITY"]
+    assert L.sa_packed_bytes(1, 128, B.SA_BF16, 8388608 - 64, ctypes.byref(n)) == 0
+    assert L.sa_packed_bytes(1, 64, B.SA_F32, 8388608, ctypes.byref(n)) == ERR["CAPACITY"]
 
 
 def ctx(**kw):
