@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 
 /* Packed context capacity (rows) must be a multiple of this (one key tile). */
 #define SA_ROW_ALIGN 64
@@ -260,6 +260,38 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
                      int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
                      void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride,
                      hipStream_t stream);
+
+/*
+ * sa_forward_ws -- sa_forward with a caller workspace that lets the bf16
+ * forward balance its last round of workgroups.
+ *
+ * The bf16 forward runs one workgroup per (head, 256-query tile) unit and one
+ * workgroup per compute unit at a time, so W units take ceil(W / n_cu)
+ * rounds. When the last round would be at most half full (1920 units on 256
+ * CUs: 7.5 rounds run as 8), its r units are computed first as 2r key halves
+ * (half a round) into the workspace, the other W - r units as usual, and the
+ * halves merged by their log-sum-exps (the identity sa_forward_split rests
+ * on): the same result as sa_forward up to rounding, in fewer rounds.
+ * workspace: device, 16-byte aligned, at least sa_forward_workspace_bytes()
+ *            bytes for this context and nq on the current device; NULL (or a
+ *            forward that gains nothing) runs exactly sa_forward. Calls that
+ *            share a workspace must not overlap.
+ * Other arguments, result and errors as sa_forward; SA_ERR_CAPACITY when a
+ * workspace is given but smaller than needed.
+ */
+sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                        int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                        void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sa_forward_workspace_bytes -- bytes of workspace sa_forward_ws uses for this
+ * context and nq on the current device (0 when it would run as sa_forward):
+ * 2 r * 256 * (head_dim + 1) * 4 for the r balanced units, at most
+ * n_cu * 256 * (head_dim + 1) * 4 (33.8 MB at head_dim 128 on 256 CUs).
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, and the context checks of sa_forward.
+ */
+sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes);
 
 /*
  * sa_forward_split -- split-KV form of sa_forward for problems with few query

@@ -93,6 +93,11 @@ def lib():
         L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
                                  ctypes.c_float, vp, i32, i64, i64, vp]
         L.sa_forward.restype = i32
+        L.sa_forward_ws.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                    ctypes.c_float, vp, i32, i64, i64, vp, ctypes.c_size_t, vp]
+        L.sa_forward_ws.restype = i32
+        L.sa_forward_workspace_bytes.argtypes = [ctypes.POINTER(Context), i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.sa_forward_workspace_bytes.restype = i32
         L.sa_forward_split.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
                                        ctypes.c_float, i32, vp, vp, vp]
         L.sa_forward_split.restype = i32
@@ -239,6 +244,36 @@ def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None
     _check("sa_forward", lib().sa_forward(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs, _ptr(q_rope),
                                           None if qn is None else ctypes.byref(qn), float(softmax_scale),
                                           _ptr(out), _DTYPES[out.dtype], ors, ohs, _stream(stream)))
+    return out
+
+
+def sa_forward_workspace_bytes(ctx, nq):
+    """Bytes of workspace ``sa_forward_ws`` uses for ``nq`` query rows over
+    ``ctx`` on the current device (0: it would run as ``sa_forward``)."""
+    n = ctypes.c_size_t()
+    c = ctx.struct()
+    _check("sa_forward_workspace_bytes", lib().sa_forward_workspace_bytes(ctypes.byref(c), int(nq), ctypes.byref(n)))
+    return n.value
+
+
+def sa_forward_ws(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None, q_norm=None,
+                  workspace=None):
+    """``sa_forward`` with a device workspace (a tensor of at least
+    ``sa_forward_workspace_bytes`` bytes, or None) that balances the last
+    round of workgroups."""
+    qrs, qhs = _rows_heads(q, "q")
+    if softmax_scale is None:
+        softmax_scale = ctx.head_dim ** -0.5
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    ors, ohs = _rows_heads(out, "out")
+    c = ctx.struct()
+    qn = None if q_norm is None else q_norm.struct()
+    ws, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check("sa_forward_ws", lib().sa_forward_ws(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs, _ptr(q_rope),
+                                                None if qn is None else ctypes.byref(qn), float(softmax_scale),
+                                                _ptr(out), _DTYPES[out.dtype], ors, ohs, ws, ws_bytes,
+                                                _stream(stream)))
     return out
 
 

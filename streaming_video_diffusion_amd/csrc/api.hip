@@ -284,11 +284,11 @@ static sa_status forward_launch(const sa_context *ctx, sa::FwdArgs &a, hipStream
     return SA_OK;
 }
 
-sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
-                     const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
-                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream) {
-    g_err[0] = 0;
-    sa::FwdArgs a;
+// Arguments of a forward that writes out (sa_forward, sa_forward_ws).
+static sa_status forward_out_args(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                                  int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm,
+                                  float softmax_scale, void *out, sa_dtype out_dtype, int64_t o_row_stride,
+                                  int64_t o_head_stride, sa::FwdArgs &a) {
     sa_status st = forward_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, a);
     if (st != SA_OK) return st;
     if (!valid_dtype(out_dtype)) return fail(SA_ERR_DTYPE, "out_dtype %d is not SA_F32 or SA_BF16", (int)out_dtype);
@@ -304,7 +304,105 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
     a.o_rs = o_row_stride;
     a.o_hs = o_head_stride;
     a.out_f32 = out_dtype == SA_F32;
+    return SA_OK;
+}
+
+sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
+                     const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
+                     sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
+                                    out_dtype, o_row_stride, o_head_stride, a);
+    if (st != SA_OK || nq == 0) return st;
     return forward_launch(ctx, a, stream);
+}
+
+// Balanced tail of the bf16 forward on the current device: one workgroup per
+// (head, query tile) unit runs per CU at a time, so W units take ceil(W /
+// n_cu) rounds; when the last round is at most half full, its r units are run
+// first as 2r key halves (half a round) and merged, then the other W - r units
+// (whole rounds).
+struct TailPlan {
+    int units = 0;       // r (0: not used)
+    int first_unit = 0;  // W - r
+};
+static TailPlan tail_plan(const sa_context *ctx, int64_t nq) {
+    TailPlan p;
+    if (ctx->dtype != SA_BF16 || nq <= 0) return p;
+    const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
+    const int64_t units = (nq + bm - 1) / bm * ctx->heads;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return p;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0) return p;
+    const int64_t rounds = (units + n_cu - 1) / n_cu;
+    const int64_t r = units - (rounds - 1) * n_cu;
+    const int64_t ntiles = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN;
+    if (rounds < 2 || 2 * r > n_cu || ntiles < 2 || units > 0x7fffffff) return p;
+    p.units = (int)r;
+    p.first_unit = (int)(units - r);
+    return p;
+}
+static size_t tail_bytes(int units, int head_dim) {
+    return (size_t)units * 2 * (size_t)sa::fwd_bf16_rows_per_workgroup() * (size_t)(head_dim + 1) * sizeof(float);
+}
+
+sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes) {
+    g_err[0] = 0;
+    if (!bytes) return fail(SA_ERR_NULL, "bytes is NULL");
+    *bytes = 0;
+    sa_status st = check_context(ctx);
+    if (st != SA_OK) return st;
+    if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
+    const TailPlan p = tail_plan(ctx, nq);
+    *bytes = p.units ? tail_bytes(p.units, ctx->head_dim) : 0;
+    return SA_OK;
+}
+
+sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
+                        const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
+                        sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
+                                    out_dtype, o_row_stride, o_head_stride, a);
+    if (st != SA_OK || nq == 0) return st;
+    const TailPlan p = tail_plan(ctx, nq);
+    if (!p.units || !workspace) return forward_launch(ctx, a, stream);
+    const size_t need = tail_bytes(p.units, ctx->head_dim);
+    if (workspace_bytes < need)
+        return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
+    float *part = static_cast<float *>(workspace);
+    float *lse = part + (size_t)p.units * 2 * bm * ctx->head_dim;
+    sa::FwdArgs t = a;  // the tail's key halves first (half a round) ...
+    t.tail_units = p.units;
+    t.tail_part = part;
+    t.tail_lse = lse;
+    hipError_t e = sa::launch_fwd_bf16(t, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch (tail)");
+    sa::FwdArgs m = a;  // ... then the whole rounds ...
+    m.grid_units = p.first_unit;
+    e = sa::launch_fwd_bf16(m, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    sa::TailCombineArgs c{};  // ... and the merge of the halves.
+    c.part = part;
+    c.lse = lse;
+    c.out = out;
+    c.nq = nq;
+    c.o_rs = o_row_stride;
+    c.o_hs = o_head_stride;
+    c.heads = ctx->heads;
+    c.n_qt = (int)((nq + bm - 1) / bm);
+    c.bm = (int)bm;
+    c.first_unit = p.first_unit;
+    c.units = p.units;
+    c.out_f32 = out_dtype == SA_F32;
+    e = sa::launch_tail_combine(c, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "tail merge launch");
+    return SA_OK;
 }
 
 sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,

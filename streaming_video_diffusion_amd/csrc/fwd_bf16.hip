@@ -148,7 +148,7 @@ struct Tile {
 
 };
 
-__device__ __forceinline__ void vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void vm_lgkm_cnt0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
 // Value of lane l ^ 32 (the other half-wave holds the same query column).
 __device__ __forceinline__ float half_swap_partner(float x) {
@@ -178,10 +178,22 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int n_qt = (int)((a.nq + BM - 1) / BM);
     // logical = (head * n_splits + split) * n_qt + query tile: the workgroups
     // of one head and key range are neighbours, so they share an XCD's L2.
-    const int hs = logical / n_qt;
-    const int qt = logical - hs * n_qt;
-    const int head = hs / a.n_splits;
-    const int split = hs - head * a.n_splits;
+    // In a balanced-tail launch, logical = 2 * unit + half instead, unit
+    // counting from the first of the last tail_units (head, query tile) units.
+    int qt, head, split, n_splits = a.n_splits, tail_unit = 0;
+    if (a.tail_units) {
+        tail_unit = logical >> 1;
+        split = logical & 1;
+        n_splits = 2;
+        const int u = n_qt * a.heads - a.tail_units + tail_unit;
+        head = u / n_qt;
+        qt = u - head * n_qt;
+    } else {
+        const int hs = logical / n_qt;
+        qt = logical - hs * n_qt;
+        head = hs / a.n_splits;
+        split = hs - head * a.n_splits;
+    }
 
     const int t = threadIdx.x;
     const int w = t >> 6;
@@ -263,8 +275,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int ntiles_all = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
     // This workgroup's key tiles [t_begin, ntiles) (all of them without split-KV).
-    const int t_begin = split_first_tile(split, a.n_splits, ntiles_all);
-    const int ntiles = split_first_tile(split + 1, a.n_splits, ntiles_all);
+    const int t_begin = split_first_tile(split, n_splits, ntiles_all);
+    const int ntiles = split_first_tile(split + 1, n_splits, ntiles_all);
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     const f32x16 zero16 = f32x16{};
     // Per-lane operand-read bases as LDS byte addresses. smem is 1024-byte
@@ -286,8 +298,11 @@ void fwd_bf16_kernel(FwdArgs a) {
     auto issue = [&](int kt) __attribute__((always_inline)) {
         if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), krs, vrs, (uint32_t)(kt * BN), wu);
     };
+    // Every LDS read of the tile has returned (lgkmcnt 0) and every load this
+    // wave issued has landed (vmcnt 0) before the barrier, so a buffer is
+    // reloaded only after every wave is done with it.
     auto end_tile = [&]() __attribute__((always_inline)) {
-        vmcnt0();
+        vm_lgkm_cnt0();
         __syncthreads();
     };
 
@@ -422,9 +437,10 @@ void fwd_bf16_kernel(FwdArgs a) {
     // 32 c + 8 g + 4 hf .. +3 of each 32-row d tile.
     auto store = [&](float lsum, float m) __attribute__((always_inline)) {
         const float inv = 1.0f / lsum;
-        if (a.partial) {  // split-KV: normalised partial output and natural log-sum-exp
-            const int64_t prow = ((int64_t)split * a.nq + q_row) * a.heads + head;
-            float *pp = a.partial + prow * D;
+        if (a.partial || a.tail_units) {  // split-KV: normalised partial output and natural log-sum-exp
+            const int64_t prow = a.tail_units ? ((int64_t)tail_unit * 2 + split) * BM + (q_row - (int64_t)qt * BM)
+                                              : ((int64_t)split * a.nq + q_row) * a.heads + head;
+            float *pp = (a.tail_units ? a.tail_part : a.partial) + prow * D;
 #pragma unroll
             for (int c = 0; c < DT; ++c)
 #pragma unroll
@@ -436,7 +452,7 @@ void fwd_bf16_kernel(FwdArgs a) {
                     r.w = o[c][4 * g + 3] * inv;
                     *reinterpret_cast<f32x4 *>(pp + 32 * c + 8 * g + 4 * hf) = r;
                 }
-            if (hf == 0) a.lse[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
+            if (hf == 0) (a.tail_units ? a.tail_lse : a.lse)[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
             return;
         }
         const int64_t obase = q_row * a.o_rs + (int64_t)head * a.o_hs;
@@ -571,7 +587,8 @@ template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     constexpr int BM = kNW * 32;
     const int64_t n_qt = (a.nq + BM - 1) / BM;
-    const int64_t nwg = n_qt * a.heads * a.n_splits;
+    const int64_t nwg = a.tail_units ? 2 * (int64_t)a.tail_units
+                                     : a.grid_units ? (int64_t)a.grid_units : n_qt * a.heads * a.n_splits;
     auto kern = fwd_bf16_kernel<D, kNW, OUT_F32>;
     constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,

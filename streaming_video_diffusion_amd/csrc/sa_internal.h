@@ -82,9 +82,31 @@ struct FwdArgs {
     int32_t n_splits;
     float *partial;
     float *lse;
+    // Grid override: launch only the first grid_units (head, query tile)
+    // units (0: all of them).
+    int32_t grid_units;
+    // Balanced tail (bf16 path): with tail_units > 0 the launch covers only the
+    // last tail_units units, each as two key halves (one workgroup each),
+    // writing normalised float32 outputs to tail_part [unit][half][BM][d] and
+    // natural log-sum-exps to tail_lse [unit][half][BM] (unit counted from the
+    // first tail unit, rows from the unit's first query row).
+    int32_t tail_units;
+    float *tail_part;
+    float *tail_lse;
 };
 // Key tiles [first, end) of split s of n over ntiles tiles (balanced, non-empty when n <= ntiles).
 __host__ __device__ inline int split_first_tile(int s, int n, int ntiles) { return (int)((int64_t)s * ntiles / n); }
+
+// --- balanced tail merge ---------------------------------------------------
+struct TailCombineArgs {
+    const float *part;  // [units][2][BM][d]
+    const float *lse;   // [units][2][BM]
+    void *out;
+    int64_t nq, o_rs, o_hs;
+    int32_t heads, n_qt, bm, first_unit, units;
+    int32_t out_f32;
+};
+hipError_t launch_tail_combine(const TailCombineArgs &a, int head_dim, hipStream_t stream);
 
 // --- split-KV combine -------------------------------------------------------
 struct CombineArgs {

@@ -68,6 +68,10 @@ class ChunkAttention:
         self.ctx = B.PackedContext(w.heads, w.head_dim, self.dtype, w.nk, device=dev)
         self.ctx.rows = w.nk
         self.out = torch.empty((w.nq, w.heads, w.head_dim), dtype=self.out_dtype, device=dev)
+        # Workspace that lets the forward balance its last round of workgroups
+        # (allocated once; None when the forward would not use it).
+        ws = B.sa_forward_workspace_bytes(self.ctx, w.nq)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
 
     def _tables(self, dynamic, stream):
         w = self.w
@@ -99,7 +103,8 @@ class ChunkAttention:
         return self.forward(stream)
 
     def forward(self, stream=None):
-        B.sa_forward(self.ctx, self.q, self.q_table, self.w.scale, out=self.out, stream=stream, q_norm=self.q_norm)
+        B.sa_forward_ws(self.ctx, self.q, self.q_table, self.w.scale, out=self.out, stream=stream,
+                        q_norm=self.q_norm, workspace=self.workspace)
         return self.out
 
     def host_inputs(self):

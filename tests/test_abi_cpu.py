@@ -50,12 +50,12 @@ def test_header_constants_match_binding():
     assert ctypes.sizeof(B.Segment) == 96
     assert ctypes.sizeof(B.Context) == 48
     assert ctypes.sizeof(B.RmsNorm) == 16
-    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 3
+    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 4
     assert int(re.search(r"#define SA_MAX_POOL (\d+)", text).group(1)) == 8
 
 
 def test_version_and_status_strings(L):
-    assert L.sa_abi_version() == 3
+    assert L.sa_abi_version() == 4
     assert L.sa_status_string(0) == b"SA_OK"
     for name, val in ERR.items():
         assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
@@ -210,6 +210,25 @@ def test_forward_errors(L):
 
 def fwd_split(L, c, nsplit=2, q=FAKE, nq=8, partial=FAKE * 4, lse=FAKE * 5, qrs=256, qhs=128):
     return L.sa_forward_split(ctypes.byref(c), q, nq, qrs, qhs, None, None, 0.1, nsplit, partial, lse, None)
+
+
+def test_forward_ws_errors(L):
+    n = ctypes.c_size_t(7)
+    assert L.sa_forward_workspace_bytes(None, 8, ctypes.byref(n)) == ERR["NULL"] and n.value == 0
+    assert L.sa_forward_workspace_bytes(ctypes.byref(ctx()), 8, None) == ERR["NULL"]
+    assert L.sa_forward_workspace_bytes(ctypes.byref(ctx()), -1, ctypes.byref(n)) == ERR["SHAPE"]
+    assert L.sa_forward_workspace_bytes(ctypes.byref(ctx(head_dim=96)), 8, ctypes.byref(n)) == ERR["UNSUPPORTED"]
+
+    def ws(c, q=FAKE, nq=8, out=FAKE * 3, odt=B.SA_BF16, ors=256):
+        return L.sa_forward_ws(None if c is None else ctypes.byref(c), q, nq, 256, 128, None, None, 0.1, out, odt,
+                               ors, 128, None, 0, None)
+    assert ws(None) == ERR["NULL"]
+    assert ws(ctx(rows=0)) == ERR["CAPACITY"]
+    assert ws(ctx(), odt=9) == ERR["DTYPE"]
+    assert ws(ctx(), out=None) == ERR["NULL"]
+    assert ws(ctx(), out=FAKE + 2) == ERR["ALIGN"]
+    assert ws(ctx(), q=None) == ERR["NULL"]
+    assert ws(ctx(), nq=0) == 0
 
 
 def test_forward_split_errors(L):

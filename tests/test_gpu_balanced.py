@@ -1,0 +1,103 @@
+"""The balanced-tail forward (sa_forward_ws): the last, at most half-full round
+of (head, query tile) units runs as key halves merged by their log-sum-exps.
+Checked against the fp64 oracle and against the plain forward, which every
+unit outside the tail must match bit for bit."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_parity, note, oracle, run, sample_rows
+from streaming_video_diffusion_amd import binding as B
+from streaming_video_diffusion_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+BM = 256  # query rows per (head, query tile) unit of the bf16 forward
+
+
+def plan(nq, heads):
+    """(units in the tail, first tail unit) as the library plans them on this GPU."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    units = math.ceil(nq / BM) * heads
+    rounds = math.ceil(units / n_cu)
+    r = units - (rounds - 1) * n_cu
+    if rounds < 2 or 2 * r > n_cu:
+        return 0, units
+    return r, units - r
+
+
+def tail_mask(nq, heads, first_unit):
+    """[nq][heads] True where the (row, head) belongs to a tail unit."""
+    n_qt = math.ceil(nq / BM)
+    m = np.zeros((nq, heads), dtype=bool)
+    for u in range(first_unit, n_qt * heads):
+        h, qt = divmod(u, n_qt)
+        m[qt * BM:min((qt + 1) * BM, nq), h] = True
+    return m
+
+
+def balanced_case():
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    heads = n_cu // 8            # 9 query tiles x n_cu/8 heads = n_cu + n_cu/8 units: a tail of n_cu/8
+    return I.custom("balanced", 600, "bf16", heads, 128, [150, 130], 9 * BM - 100, prompt_rows=20)
+
+
+def test_workspace_bytes_follow_the_rounds():
+    for w in (I.full_1344x768(), I.lowres_bf16(), balanced_case()):
+        ctx = B.PackedContext(w.heads, w.head_dim, torch.bfloat16, w.nk)
+        ctx.rows = w.nk
+        r, _ = plan(w.nq, w.heads)
+        assert B.sa_forward_workspace_bytes(ctx, w.nq) == 2 * r * BM * (w.head_dim + 1) * 4, w.name
+
+
+@pytest.mark.parametrize("out_dtype", [None, torch.float32], ids=["out_bf16", "out_f32"])
+def test_balanced_small_full(out_dtype):
+    w = balanced_case()
+    r, first = plan(w.nq, w.heads)
+    assert r > 0
+    ca, out = run(w, out_dtype=out_dtype)
+    assert ca.workspace is not None
+    rel, mx = assert_parity(out, oracle(ca), "bf16", w.name)
+    note(f"  {w.name}: tail of {r} units, rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale, out_dtype=ca.out_dtype)
+    torch.cuda.synchronize()
+    keep = torch.from_numpy(~tail_mask(w.nq, w.heads, first)).cuda()
+    assert torch.equal(plain[keep], ca.out[keep]), "units outside the tail must match the plain forward"
+
+
+def test_no_workspace_is_the_plain_forward():
+    w = balanced_case()
+    ca, _ = run(w)
+    a = B.sa_forward_ws(ca.ctx, ca.q, ca.q_table, w.scale, workspace=None)
+    b = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_small_workspace_is_rejected():
+    w = balanced_case()
+    ca, _ = run(w)
+    need = B.sa_forward_workspace_bytes(ca.ctx, w.nq)
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.SaError) as e:
+        B.sa_forward_ws(ca.ctx, ca.q, ca.q_table, w.scale, workspace=small)
+    assert e.value.status == -5
+
+
+def test_balanced_full_size_tail_rows():
+    """1344x768: the tail is the last units (the last heads); sampled rows of every head."""
+    w = I.full_1344x768()
+    r, first = plan(w.nq, w.heads)
+    ca, out = run(w)
+    note(f"  tail of {r} units from unit {first}")
+    rows = sample_rows(w.nq, seed=11)
+    rel, mx = assert_parity(out[rows], oracle(ca, rows=rows), "bf16", w.name)
+    note(f"  rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    if r:
+        plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale).float().cpu().numpy()
+        torch.cuda.synchronize()
+        m = tail_mask(w.nq, w.heads, first)
+        assert np.array_equal(plain[~m], out[~m])
