@@ -7,9 +7,11 @@ timing), and the forward pass. Inputs are resident in HBM before timing.
 
 Prints ONE JSON line. ``value`` is attention TFLOP/s over the whole step
 (4*Nq*Nk*d*H flops per chunk / step time); ``ms_per_step`` is ms per chunk.
-``roofline`` prices the forward kernel (the dominant kernel) from HIP events
-around each of its launches in the timed region; ``cpu_baseline`` times the
-fp64 oracle on a bounded sample of the same workload on the host cores.
+``roofline`` prices the forward (the dominant kernel: its launch over the
+balanced tail's key halves, its launch over the other units, and their merge)
+from HIP events around each forward in the timed region; ``cpu_baseline``
+times the fp64 oracle on a bounded sample of the same workload on the host
+cores.
 """
 
 import argparse
@@ -25,16 +27,18 @@ METRIC = "attention TFLOP/s + ms/chunk at 1344x768 (12096 q x 28480 kv, 40 heads
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (published)
 FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf16.hip")
-FWD_KERNEL = "fwd_bf16_kernel<128, 8, false>"
-# HBM traffic of one forward launch at 1344x768, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE (KiB per dispatch; profiles/fwd_bf16_1344x768_hbm_traffic.txt),
-# each scaled by what the same counter reads for a plain device copy of known
-# size (FETCH_SIZE counts 0.5x the bytes read, WRITE_SIZE 1.0x the bytes
-# written). Valid only for the forward source these counters were taken on.
+FWD_KERNEL = "fwd_bf16_kernel<128, 8, false> (balanced: tail halves + main grid) + tail_combine_kernel<128, false>"
+# HBM traffic of one forward at 1344x768 (its three dispatches: the forward
+# kernel over the balanced tail's key halves, over the other units, and the
+# merge), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB, summed over the
+# three; profiles/fwd_bf16_1344x768_hbm_traffic.txt), each scaled by what the
+# same counter reads for a plain device copy of known size (FETCH_SIZE counts
+# 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written). Valid only for the
+# forward source these counters were taken on.
 TRAFFIC = {
-    "source_sha256": "e895560b1f52c9c5caeca2d1a3f9f8718bd575ef01117931de55ea41545b0aef",
-    "fetch_kib": 751461.5,
-    "write_kib": 120964.9,
+    "source_sha256": "258d4ca44980a83677da9fbe195acc7dca801c5dbac93bdd254f6c293b814b9c",
+    "fetch_kib": 790118.0,
+    "write_kib": 153440.5,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
