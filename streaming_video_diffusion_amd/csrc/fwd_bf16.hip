@@ -376,7 +376,9 @@ void fwd_bf16_kernel(FwdArgs a) {
     // tile's Q.K^T (K operands read two steps ahead) interleaved with its
     // exponentials, then its four P.V products. Every operand read is issued
     // several matrix-core ops before its use, so LDS latency stays hidden;
-    // sched_barrier pins the order.
+    // sched_barrier pins the order. The wave raises its issue priority while
+    // it issues matrix-core ops, so the SIMD's other wave, when it has VALU
+    // work, does not hold them back (the matrix core stays fed).
     auto qk_exp_pv = [&](const unsigned char *nbuf, f32x16 (&sn)[2], const unsigned char *buf,
                          const f32x16 (&s)[2]) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
@@ -411,8 +413,10 @@ void fwd_bf16_kernel(FwdArgs a) {
                     kr[j + 2][0] = kread(j + 2, 0);
                     kr[j + 2][1] = kread(j + 2, 1);
                 }
+                __builtin_amdgcn_s_setprio(1);
                 sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][0], qreg[j], j ? sn[0] : zero16, 0, 0, 0);
                 sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][1], qreg[j], j ? sn[1] : zero16, 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
                 // this k-step's share of the group's exponentials
                 constexpr int E = 8 / KSTEPS_PER_GROUP;
 #pragma unroll
@@ -426,8 +430,10 @@ void fwd_bf16_kernel(FwdArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int c = 0; c < DT; ++c) o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c], pv, o[c], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
         l += ls[0] + ls[1];
