@@ -12,7 +12,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamattn.so")
+# The in-tree library; STREAMATTN_LIB may name another build of it (a variant).
+LIB_PATH = os.environ.get("STREAMATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libstreamattn.so")
 
 SA_OK = 0
 SA_F32 = 0
@@ -154,6 +156,12 @@ def packed_bytes(heads, head_dim, dtype, capacity_rows):
     return n.value
 
 
+def rotates_k_in_forward():
+    """True for a library built to rotate bf16 keys in the forward's key-tile
+    load (its packed K buffers also hold a per-row rotary table)."""
+    return packed_bytes(1, 128, torch.bfloat16, SA_ROW_ALIGN) > SA_ROW_ALIGN * 128 * 2
+
+
 def padded_rows(rows):
     """Smallest legal capacity (multiple of SA_ROW_ALIGN) holding ``rows``."""
     return (rows + SA_ROW_ALIGN - 1) // SA_ROW_ALIGN * SA_ROW_ALIGN
@@ -182,6 +190,14 @@ class PackedContext:
         self.heads, self.head_dim, self.dtype = heads, head_dim, dtype
         self.capacity_rows = cap
         self.rows = 0
+
+    def k_data(self):
+        """The packed key elements (without a rotate-in-forward build's row tables)."""
+        return self.k_packed[:self.heads * self.capacity_rows * self.head_dim]
+
+    def v_data(self):
+        """The packed value elements."""
+        return self.v_packed[:self.heads * self.capacity_rows * self.head_dim]
 
     def struct(self):
         return Context(self.heads, self.head_dim, _DTYPES[self.dtype], self.capacity_rows, self.rows,

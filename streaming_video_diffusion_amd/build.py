@@ -32,12 +32,19 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every csrc/*.hip into libstreamattn.so (always recompiles)."""
+def build(verbose=False, extra_flags=(), lib_path=LIB):
+    """Compile every csrc/*.hip into libstreamattn.so (always recompiles).
+
+    ``extra_flags`` such as ``-DSA_ROTATE_K_IN_FORWARD=1`` (keys rotated in
+    the forward's key-tile load instead of the pack) build a variant, usually
+    with its own ``lib_path``; the binding loads a variant named by the
+    STREAMATTN_LIB environment variable.
+    """
     srcs = sources()
     if not srcs:
         raise RuntimeError(f"no HIP sources under {CSRC}")
-    fd, tmp = tempfile.mkstemp(suffix=".so", dir=PKG, prefix=".libstreamattn.")
+    out_dir = os.path.dirname(os.path.abspath(lib_path))
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=out_dir, prefix=".libstreamattn.")
     os.close(fd)
     cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", tmp]
     if verbose:
@@ -51,9 +58,16 @@ def build(verbose=False, extra_flags=()):
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--rotate-k-in-forward", action="store_true",
+                    help="variant: keys rotated in the forward's key-tile load, not in the pack")
+    ap.add_argument("--out", default=LIB, help="library path to write")
+    args = ap.parse_args()
+    flags = ("-DSA_ROTATE_K_IN_FORWARD=1",) if args.rotate_k_in_forward else ()
+    print(build(verbose=True, extra_flags=flags, lib_path=args.out))

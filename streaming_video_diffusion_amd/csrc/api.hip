@@ -149,6 +149,7 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
                     "capacity_rows %lld is not a multiple of %d with one head's K/V below 2^31 bytes",
                     (long long)capacity_rows, SA_ROW_ALIGN);
     *bytes_each = (size_t)heads * (size_t)capacity_rows * (size_t)head_dim * (size_t)elem_bytes(dtype);
+    if (SA_ROTATE_K_IN_FORWARD && dtype == SA_BF16) *bytes_each += sa::k_table_bytes(capacity_rows, head_dim);
     return SA_OK;
 }
 
@@ -165,6 +166,9 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
     sa::PackArgs a{};
     a.k_packed = ctx->k_packed;
     a.v_packed = ctx->v_packed;
+    if (SA_ROTATE_K_IN_FORWARD && ctx->dtype == SA_BF16)
+        a.k_table = reinterpret_cast<float *>(static_cast<unsigned char *>(ctx->k_packed) +
+                                              sa::k_table_offset_bytes(ctx->heads, ctx->capacity_rows, ctx->head_dim));
     a.cap = ctx->capacity_rows;
     a.heads = ctx->heads;
     int64_t max_tiles = 0;
@@ -262,6 +266,9 @@ static sa_status forward_args(const sa_context *ctx, const void *q, int64_t nq, 
     a.q_rope = q_rope;
     a.k = ctx->k_packed;
     a.v = ctx->v_packed;
+    if (SA_ROTATE_K_IN_FORWARD && ctx->dtype == SA_BF16)
+        a.k_table = reinterpret_cast<const float *>(static_cast<const unsigned char *>(ctx->k_packed) +
+                                                    sa::k_table_offset_bytes(ctx->heads, ctx->capacity_rows, ctx->head_dim));
     a.q_rs = q_row_stride;
     a.q_hs = q_head_stride;
     a.nq = nq;

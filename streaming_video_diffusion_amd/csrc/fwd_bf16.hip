@@ -158,7 +158,7 @@ __device__ __forceinline__ float half_swap_partner(float x) {
     return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
 }
 
-template <int D, int NW, bool OUT_F32>
+template <int D, int NW, bool OUT_F32, bool ROTK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdArgs a) {
     constexpr int BM = NW * 32;  // queries per workgroup (32 per wave)
@@ -304,6 +304,39 @@ void fwd_bf16_kernel(FwdArgs a) {
     auto end_tile = [&]() __attribute__((always_inline)) {
         vm_lgkm_cnt0();
         __syncthreads();
+    };
+
+    // Rotate-in-forward (ROTK): the keys of tile kt sit unrotated in its LDS
+    // buffer; the workgroup rotates them in place from the per-row tables
+    // (one bf16 rounding), then meets a barrier that waits for LDS only, so
+    // the tile loads in flight keep going. Its table loads are issued before
+    // the next tile loads, so waiting for them never waits for those.
+    auto rotate_k = [&](int kt_r) __attribute__((always_inline)) {
+        if (kt_r < ntiles) {
+            unsigned char *b = buf_of(kt_r);
+            const float *tbl = a.k_table + (int64_t)kt_r * BN * D;
+#pragma unroll
+            for (int i = t; i < BN * (D / 8); i += NW * 64) {
+                const int r = i / (D / 8), c = i % (D / 8);
+                bf16x8 *p = reinterpret_cast<bf16x8 *>(b + T::koff(r, c));
+                const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tbl + (r * (D / 2) + 4 * c) * 2);
+                const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tbl + (r * (D / 2) + 4 * c) * 2 + 4);
+                const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+                const bf16x8 x = *p;
+                bf16x8 y;
+#pragma unroll
+                for (int pr = 0; pr < 4; ++pr) {
+                    const float x0 = (float)x[2 * pr], x1 = (float)x[2 * pr + 1];
+                    y[2 * pr] = (bf16)(x0 * cs[2 * pr] - x1 * cs[2 * pr + 1]);
+                    y[2 * pr + 1] = (bf16)(x0 * cs[2 * pr + 1] + x1 * cs[2 * pr]);
+                }
+                *p = y;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
 
     // S^T (log2 units) minus the seed: K Q^T + seed, for the tile in buf.
@@ -500,13 +533,16 @@ void fwd_bf16_kernel(FwdArgs a) {
     // Two score sets alternate roles (unrolled by two), so no copy of the
     // next tile's scores is needed between tiles.
     f32x16 s[2], sb[2];
+    if constexpr (ROTK) rotate_k(t_begin);
     qk(buf_of(t_begin), s, zero16);
     int kt = t_begin;
     for (; kt + 1 < ntiles; kt += 2) {
+        if constexpr (ROTK) rotate_k(kt + 1);
         issue(kt + 2);
         mask(s, kt);
         qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
         end_tile();
+        if constexpr (ROTK) rotate_k(kt + 2);
         issue(kt + 3);
         mask(sb, kt + 1);
         qk_exp_pv(buf_of(kt + 2), s, buf_of(kt + 1), sb);
@@ -515,6 +551,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     if (kt < ntiles) {
         // Last (odd) tile: the next-tile scores read a resident buffer and are
         // discarded.
+        if constexpr (ROTK) rotate_k(kt + 1);
         issue(kt + 2);
         mask(s, kt);
         qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
@@ -562,6 +599,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         issue(t_begin + 1);
         end_tile();
         for (int kt = t_begin; kt < ntiles; ++kt) {
+            if constexpr (ROTK) rotate_k(kt);
             issue(kt + 2);
             qk(buf_of(kt), s, zero16);
             mask(s, kt);
@@ -595,7 +633,7 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     const int64_t n_qt = (a.nq + BM - 1) / BM;
     const int64_t nwg = a.tail_units ? 2 * (int64_t)a.tail_units
                                      : a.grid_units ? (int64_t)a.grid_units : n_qt * a.heads * a.n_splits;
-    auto kern = fwd_bf16_kernel<D, kNW, OUT_F32>;
+    auto kern = a.k_table ? fwd_bf16_kernel<D, kNW, OUT_F32, true> : fwd_bf16_kernel<D, kNW, OUT_F32, false>;
     constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,
     // idempotent, no stream work).

@@ -141,7 +141,21 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
             vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
         }
         if (s.norm.on) norm_row<CH, 8>(x, s.norm, h, D, chunk * 8);
-        if (s.rope) {
+        if (a.k_table) {
+            // keys stay unrotated; head 0's workgroup records the row's table
+            // entries for this chunk's 4 pairs (identity without rotation)
+            if (h == 0) {
+                f32x4 t0 = {1.f, 0.f, 1.f, 0.f}, t1 = {1.f, 0.f, 1.f, 0.f};
+                if (s.rope) {
+                    const f32x4 *tb = reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 4) * 2);
+                    t0 = tb[0];
+                    t1 = tb[1];
+                }
+                f32x4 *kt = reinterpret_cast<f32x4 *>(a.k_table + (row * (D / 2) + chunk * 4) * 2);
+                kt[0] = t0;
+                kt[1] = t1;
+            }
+        } else if (s.rope) {
             const f32x4 *tb = reinterpret_cast<const f32x4 *>(s.rope + (sr * (D / 2) + chunk * 4) * 2);
             const f32x4 t0 = tb[0], t1 = tb[1];
             const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
@@ -251,6 +265,8 @@ __global__ __launch_bounds__(kThreads) void zero_pad_kernel(PackArgs a, int64_t 
     const int t = threadIdx.x;
     const int64_t n = pad_end - rows;
     if (is_bf16) {
+        if (a.k_table && h == 0)  // identity tables for the padding rows
+            for (int64_t e = t; e < n * D; e += kThreads) a.k_table[rows * D + e] = (e & 1) ? 0.0f : 1.0f;
         bf16 *kp = reinterpret_cast<bf16 *>(a.k_packed) + (int64_t)h * a.cap * D;
         bf16 *vp = reinterpret_cast<bf16 *>(a.v_packed) + (int64_t)h * D * a.cap;
         for (int64_t e = t; e < n * D; e += kThreads) kp[(rows + e / D) * D + e % D] = (bf16)0.0f;

@@ -7,7 +7,23 @@
 
 #include "streamattn.h"
 
+// Where packed keys are rotated. 0 (default): once, in the pack's key load.
+// 1: the pack keeps bf16 keys unrotated and writes a per-row rotary table
+// after the key rows of k_packed; the forward rotates each key tile in LDS
+// (the rotation inside the forward's key-tile load). f32 contexts always
+// rotate in the pack.
+#ifndef SA_ROTATE_K_IN_FORWARD
+#define SA_ROTATE_K_IN_FORWARD 0
+#endif
+
 namespace sa {
+
+// Rotate-in-forward layout: float32 [capacity][head_dim/2][2] (cos, sin) per
+// packed row, starting right after the key rows of every head.
+inline size_t k_table_offset_bytes(int heads, int64_t cap, int head_dim) {
+    return (size_t)heads * (size_t)cap * (size_t)head_dim * 2;
+}
+inline size_t k_table_bytes(int64_t cap, int head_dim) { return (size_t)cap * (size_t)head_dim * sizeof(float); }
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -52,6 +68,7 @@ struct PackSeg {
 struct PackArgs {
     void *k_packed;
     void *v_packed;
+    float *k_table;  // rotate-in-forward: per-row tables to write (keys then stay unrotated); else null
     int64_t cap;
     int32_t heads;
     int32_t n_segs;
@@ -68,6 +85,7 @@ struct FwdArgs {
     const float *q_rope;
     const void *k;   // packed K
     const void *v;   // packed V
+    const float *k_table;  // rotate-in-forward: per-row tables of the packed (unrotated) keys; else null
     void *out;
     int64_t q_rs, q_hs, o_rs, o_hs;
     int64_t nq, nk, cap;

@@ -57,13 +57,25 @@ def test_pack_bf16_layout_and_rotation(d):
     note(f"[gpu] pack bf16 d={d}")
     w, ca = _pack_case("bf16", d=d)
     cap, H = ca.ctx.capacity_rows, w.heads
-    kp = ca.ctx.k_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).float().cpu().numpy().astype(np.float64)
-    vp = unpack_v_bf16(ca.ctx.v_packed, H, d, cap, w.nk).float().cpu().numpy()
+    kp = ca.ctx.k_data().view(H, cap, d)[:, :w.nk].permute(1, 0, 2).float().cpu().numpy().astype(np.float64)
+    vp = unpack_v_bf16(ca.ctx.v_data(), H, d, cap, w.nk).float().cpu().numpy()
     q, _, segs = ca.host_inputs()
+    rot_in_fwd = B.rotates_k_in_forward()
+    if rot_in_fwd:  # keys stay unrotated; a per-row (cos, sin) table follows the key rows of every head
+        tbl = ca.ctx.k_packed.view(torch.uint8)[H * cap * d * 2:].view(torch.float32).view(cap, d // 2, 2)
+        tbl = tbl.cpu().numpy().astype(np.float64)
     row = 0
     for (k, v, pos), s in zip(segs, w.segments):
-        ref = k.astype(np.float64) if pos is None else rope64.rotate(k, rope64.angles(pos, w.axis_dims, w.theta))
         got = kp[row:row + s.rows]
+        if rot_in_fwd:
+            assert np.array_equal(got, k), f"{s.name}: keys must be stored unrotated"
+            phi = np.zeros((s.rows, d // 2)) if pos is None else rope64.angles(pos, w.axis_dims, w.theta)
+            assert np.max(np.abs(tbl[row:row + s.rows, :, 0] - np.cos(phi))) <= 6e-8
+            assert np.max(np.abs(tbl[row:row + s.rows, :, 1] - np.sin(phi))) <= 6e-8
+            assert np.array_equal(vp[row:row + s.rows], v), f"{s.name}: V must be copied bit-exactly"
+            row += s.rows
+            continue
+        ref = k.astype(np.float64) if pos is None else rope64.rotate(k, rope64.angles(pos, w.axis_dims, w.theta))
         # one rounding to bf16 of an fp32-computed rotation: <= 2^-8 relative (+ fp32 slack)
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), s.name
         if pos is None:
@@ -72,12 +84,12 @@ def test_pack_bf16_layout_and_rotation(d):
         row += s.rows
     # padding rows [nk, next multiple of 64) are zeroed; rows past them are never written
     pad_end = (w.nk + 63) // 64 * 64
-    assert torch.equal(ca.ctx.k_packed.view(H, cap, d)[:, w.nk:pad_end].float(),
+    assert torch.equal(ca.ctx.k_data().view(H, cap, d)[:, w.nk:pad_end].float(),
                        torch.zeros((H, pad_end - w.nk, d), device="cuda"))
-    vt = ca.ctx.v_packed.view(H, d, cap)
+    vt = ca.ctx.v_data().view(H, d, cap)
     cols = [16 * (r // 16) + perm16(r % 16) for r in range(w.nk, pad_end)]
     assert torch.equal(vt[:, :, cols].float(), torch.zeros((H, d, len(cols)), device="cuda"))
-    assert torch.isnan(ca.ctx.k_packed.view(H, cap, d)[:, pad_end:].float()).all()
+    assert torch.isnan(ca.ctx.k_data().view(H, cap, d)[:, pad_end:].float()).all()
 
 
 def test_pack_f32_layout_and_rotation():
@@ -88,8 +100,8 @@ def test_pack_f32_layout_and_rotation():
     for buf in (ca.ctx.k_packed, ca.ctx.v_packed):
         assert torch.equal(buf.view(H, cap, d)[:, w.nk:pad_end], torch.zeros((H, pad_end - w.nk, d), device="cuda"))
         assert torch.isnan(buf.view(H, cap, d)[:, pad_end:]).all()
-    kp = ca.ctx.k_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy().astype(np.float64)
-    vp = ca.ctx.v_packed.view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy()
+    kp = ca.ctx.k_data().view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy().astype(np.float64)
+    vp = ca.ctx.v_data().view(H, cap, d)[:, :w.nk].permute(1, 0, 2).cpu().numpy()
     _, _, segs = ca.host_inputs()
     row = 0
     for (k, v, pos), s in zip(segs, w.segments):
@@ -107,7 +119,7 @@ def test_dynamic_repack_leaves_static_rows_untouched():
     ca.pack_static()
     ca.step()
     torch.cuda.synchronize()
-    k0, v0 = ca.ctx.k_packed.clone(), ca.ctx.v_packed.clone()
+    k0, v0 = ca.ctx.k_data().clone(), ca.ctx.v_data().clone()
     n_static = sum(s.rows for s in w.segments if not s.dynamic)
     for s in ca.segs:
         if s["dynamic"]:
@@ -116,11 +128,11 @@ def test_dynamic_repack_leaves_static_rows_untouched():
     ca.step()
     torch.cuda.synchronize()
     H, d, cap = w.heads, w.head_dim, ca.ctx.capacity_rows
-    kv0, kv1 = k0.view(H, cap, d), ca.ctx.k_packed.view(H, cap, d)
+    kv0, kv1 = k0.view(H, cap, d), ca.ctx.k_data().view(H, cap, d)
     assert torch.equal(kv0[:, :n_static], kv1[:, :n_static])
     assert torch.equal(-kv0[:, n_static:w.nk], kv1[:, n_static:w.nk])
     v0u = unpack_v_bf16(v0, H, d, cap, w.nk)
-    v1u = unpack_v_bf16(ca.ctx.v_packed, H, d, cap, w.nk)
+    v1u = unpack_v_bf16(ca.ctx.v_data(), H, d, cap, w.nk)
     assert torch.equal(v0u[:n_static], v1u[:n_static])
     assert not torch.equal(v0u[n_static:], v1u[n_static:])
 
@@ -133,7 +145,7 @@ def test_segment_split_gives_identical_packing():
     ca.pack_static()
     ca.step()
     torch.cuda.synchronize()
-    ref_k, ref_v, ref_o = ca.ctx.k_packed.clone(), ca.ctx.v_packed.clone(), ca.out.clone()
+    ref_k, ref_v, ref_o = ca.ctx.k_data().clone(), ca.ctx.v_data().clone(), ca.out.clone()
     hist = next(s for s in ca.segs if s["name"] == "history")
     ca.ctx.k_packed.zero_()
     ca.ctx.v_packed.zero_()
@@ -150,6 +162,6 @@ def test_segment_split_gives_identical_packing():
     torch.cuda.synchronize()
     H, d, cap = w.heads, w.head_dim, ca.ctx.capacity_rows
     # rows past ctx.rows are never written by any pack call: compare rows [0, nk)
-    assert torch.equal(ca.ctx.k_packed.view(H, cap, d)[:, :w.nk], ref_k.view(H, cap, d)[:, :w.nk])
-    assert torch.equal(unpack_v_bf16(ca.ctx.v_packed, H, d, cap, w.nk), unpack_v_bf16(ref_v, H, d, cap, w.nk))
+    assert torch.equal(ca.ctx.k_data().view(H, cap, d)[:, :w.nk], ref_k.view(H, cap, d)[:, :w.nk])
+    assert torch.equal(unpack_v_bf16(ca.ctx.v_data(), H, d, cap, w.nk), unpack_v_bf16(ref_v, H, d, cap, w.nk))
     assert torch.equal(out, ref_o)
