@@ -40,13 +40,6 @@ namespace sa {
 
 namespace {
 
-#ifndef SA_FWD_HAND
-#define SA_FWD_HAND 1
-#endif
-#ifndef SA_FWD_SGB
-#define SA_FWD_SGB 0
-#endif
-
 constexpr int BN = 64;                // keys per tile
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
@@ -622,10 +615,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
-#ifndef SA_FWD_WAVES
-#define SA_FWD_WAVES 8
-#endif
-constexpr int kNW = SA_FWD_WAVES;
+constexpr int kNW = 8;  // waves per workgroup (two per SIMD), 32 queries each
 
 template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
