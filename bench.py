@@ -36,9 +36,9 @@ FWD_KERNEL = "fwd_bf16_kernel<128, 8, false, false> (balanced: tail halves + mai
 # 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written). Valid only for the
 # forward source these counters were taken on.
 TRAFFIC = {
-    "source_sha256": "1a0f04e5af0c041b5d4f42700aba29bf18fbd56e7f7bd791cf376916ab14935b",
-    "fetch_kib": 790391.4,
-    "write_kib": 153441.8,
+    "source_sha256": "0253973aa4e5dbdd8daa360bcd4995d4af3fe8361170545f2259529fb2579c77",
+    "fetch_kib": 790336.4,
+    "write_kib": 153438.1,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
