@@ -210,6 +210,56 @@ def other_workloads(steps, skip):
     return res
 
 
+class SclkSampler:
+    """Samples the shader clock the driver reports (the line marked '*' in
+    the DRM device's pp_dpm_sclk) every ``period`` seconds on a host thread,
+    while the GPU runs the timed steps. Reports nothing where the file is
+    absent or unreadable."""
+
+    def __init__(self, period=0.01):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for path in self.paths:
+            try:
+                with open(path) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            mhz = line.split(":", 1)[1].strip().split()[0].lower().replace("mhz", "")
+                            return float(mhz)
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "source": "pp_dpm_sclk (driver-reported current shader clock), sampled during the timed steps"}
+
+
 def main():
     args = parse()
     if args.copy_calibration_mib:
@@ -243,20 +293,21 @@ def main():
     fwd_ev, pack_ev = [], []
     start, end = ev(), ev()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        for ca in calls:
-            p0, p1, f1 = ev(), ev(), ev()
-            p0.record(stream)
-            ca._tables(True, stream)
-            ca._pack(True, stream)
-            p1.record(stream)
-            ca.forward(stream)
-            f1.record(stream)
-            pack_ev.append((p0, p1))
-            fwd_ev.append((p1, f1))
-    end.record(stream)
-    torch.cuda.synchronize()
+    with SclkSampler() as sclk:
+        start.record(stream)
+        for _ in range(args.steps):
+            for ca in calls:
+                p0, p1, f1 = ev(), ev(), ev()
+                p0.record(stream)
+                ca._tables(True, stream)
+                ca._pack(True, stream)
+                p1.record(stream)
+                ca.forward(stream)
+                f1.record(stream)
+                pack_ev.append((p0, p1))
+                fwd_ev.append((p1, f1))
+        end.record(stream)
+        torch.cuda.synchronize()
 
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
@@ -296,6 +347,7 @@ def main():
         "forward_ms_median": fwd_sorted[len(fwd_sorted) // 2],
         "forward_tflops": achieved,
         "pack_tables_ms_avg": sum(pack_ms) / len(pack_ms),
+        "sclk": sclk.summary(),
         "roofline": {
             "bound": "mfma" if bf16 else "alu",
             "kernel": FWD_KERNEL if bf16 else "fwd_f32_kernel",

@@ -171,7 +171,6 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
                                               sa::k_table_offset_bytes(ctx->heads, ctx->capacity_rows, ctx->head_dim));
     a.cap = ctx->capacity_rows;
     a.heads = ctx->heads;
-    int64_t max_tiles = 0;
     int used = 0;
     for (int i = 0; i < n_segs; ++i) {
         const sa_segment &s = segs[i];
@@ -228,11 +227,11 @@ sa_status sa_pack_context(const sa_context *ctx, const sa_segment *segs, int32_t
         p.dst_row = s.dst_row;
         const int64_t tiles =
             (s.dst_row + s.rows - 1) / sa::kPackTileRows - s.dst_row / sa::kPackTileRows + 1;
-        if (tiles > max_tiles) max_tiles = tiles;
+        a.tile0[used] = a.tile0[used - 1] + tiles;
     }
     a.n_segs = used;
     if (used == 0) return SA_OK;
-    hipError_t e = sa::launch_pack(a, ctx->head_dim, ctx->dtype, max_tiles, stream);
+    hipError_t e = sa::launch_pack(a, ctx->head_dim, ctx->dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "pack launch");
     const int64_t pad_end = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN * SA_ROW_ALIGN;
     e = sa::launch_zero_pad(a, ctx->head_dim, ctx->dtype, ctx->rows, pad_end, stream);

@@ -102,6 +102,30 @@ __device__ __forceinline__ bool tile_range(const PackSeg &s, int64_t tx, TileRan
     return true;
 }
 
+// Work unit of this workgroup: segment, tile within it and head. Units come
+// in blocks of kPackBlockTiles consecutive tiles (over all segments) times all
+// heads, head-major inside a block. Dispatch ids go round-robin over the 8
+// XCDs, and block k runs on XCD k mod 8: the heads of a tile share one XCD's
+// L2, so the rows' rotation tables are fetched once per tile rather than once
+// per head and the source rows are read whole, while heavy blocks (pooled
+// tiers read s^2 source rows per packed row) still spread over all XCDs.
+// Returns false for the padding units of the last blocks.
+__device__ __forceinline__ bool pack_unit(const PackArgs &a, int &seg, int64_t &tx, int &h) {
+    const int xcd = blockIdx.x & 7;
+    const int64_t slot = blockIdx.x >> 3;
+    const int64_t per_block = (int64_t)kPackBlockTiles * a.heads;
+    const int64_t blk = a.block_base + xcd + 8 * (slot / per_block);
+    const int64_t w = slot % per_block;
+    const int hh = (int)(w / kPackBlockTiles);
+    const int64_t g = blk * kPackBlockTiles + (w - (int64_t)hh * kPackBlockTiles);
+    if (g >= a.tile0[a.n_segs]) return false;
+    h = hh;
+    seg = 0;
+    while (seg + 1 < a.n_segs && g >= a.tile0[seg + 1]) ++seg;
+    tx = g - a.tile0[seg];
+    return true;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
     constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -109,10 +133,12 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
     constexpr int PITCH = D + 8;           // LDS row pitch (elements)
     __shared__ __align__(16) bf16 sv[kPackTileRows * PITCH];
 
-    const PackSeg s = a.seg[blockIdx.z];
+    int si, h;
+    int64_t tx;
+    if (!pack_unit(a, si, tx, h)) return;
+    const PackSeg &s = a.seg[si];
     TileRange r;
-    if (!tile_range(s, blockIdx.x, r)) return;
-    const int h = blockIdx.y;
+    if (!tile_range(s, tx, r)) return;
     const int t = threadIdx.x;
     const int chunk = t % CH;
 
@@ -212,10 +238,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
     constexpr int CH = D / 4;           // 16-byte chunks per row (4 floats, 2 pairs)
     constexpr int RPP = kThreads / CH;  // rows per pass
-    const PackSeg s = a.seg[blockIdx.z];
+    int si, h;
+    int64_t tx;
+    if (!pack_unit(a, si, tx, h)) return;
+    const PackSeg &s = a.seg[si];
     TileRange r;
-    if (!tile_range(s, blockIdx.x, r)) return;
-    const int h = blockIdx.y;
+    if (!tile_range(s, tx, r)) return;
     const int t = threadIdx.x;
     const int chunk = t % CH;
     float *kp = reinterpret_cast<float *>(a.k_packed) + ((int64_t)h * a.cap) * D;
@@ -300,21 +328,31 @@ hipError_t launch_zero_pad(const PackArgs &a, int head_dim, sa_dtype dtype, int6
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream) {
-    if (a.n_segs == 0 || max_tiles == 0) return hipSuccess;
-    const dim3 grid((unsigned)max_tiles, (unsigned)a.heads, (unsigned)a.n_segs);
-    if (dtype == SA_BF16) {
-        if (head_dim == 128)
-            hipLaunchKernelGGL(pack_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL(pack_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, a);
-    } else {
-        if (head_dim == 128)
-            hipLaunchKernelGGL(pack_f32_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL(pack_f32_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+hipError_t launch_pack(const PackArgs &args, int head_dim, sa_dtype dtype, hipStream_t stream) {
+    const int64_t blocks = (args.tile0[args.n_segs] + kPackBlockTiles - 1) / kPackBlockTiles;
+    const int64_t per_block = (int64_t)kPackBlockTiles * args.heads;
+    // whole rounds of 8 blocks (one per XCD), at most about 2^30 workgroups per launch
+    const int64_t max_rounds = ((int64_t(1) << 30) / (8 * per_block)) > 0 ? (int64_t(1) << 30) / (8 * per_block) : 1;
+    PackArgs a = args;
+    for (a.block_base = 0; a.block_base < blocks; a.block_base += 8 * max_rounds) {
+        const int64_t left = (blocks - a.block_base + 7) / 8;
+        const int64_t rounds = left < max_rounds ? left : max_rounds;
+        const dim3 grid((unsigned)(rounds * 8 * per_block));
+        if (dtype == SA_BF16) {
+            if (head_dim == 128)
+                hipLaunchKernelGGL(pack_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL(pack_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+        } else {
+            if (head_dim == 128)
+                hipLaunchKernelGGL(pack_f32_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL(pack_f32_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sa

@@ -73,9 +73,14 @@ struct PackArgs {
     int32_t heads;
     int32_t n_segs;
     PackSeg seg[SA_MAX_SEGMENTS];
+    // Segment i holds the pack's global tiles [tile0[i], tile0[i+1]) (64-row
+    // tiles of the packed row space, counted over the segments in order).
+    int64_t tile0[SA_MAX_SEGMENTS + 1];
+    int64_t block_base;  // first tile block of this launch (set by launch_pack)
 };
-constexpr int kPackTileRows = 64;  // packed rows per pack workgroup
-hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t max_tiles, hipStream_t stream);
+constexpr int kPackTileRows = 64;   // packed rows per pack workgroup
+constexpr int kPackBlockTiles = 2;  // tiles per block of pack work units
+hipError_t launch_pack(const PackArgs &a, int head_dim, sa_dtype dtype, hipStream_t stream);
 hipError_t launch_zero_pad(const PackArgs &a, int head_dim, sa_dtype dtype, int64_t rows, int64_t pad_end,
                            hipStream_t stream);
 
