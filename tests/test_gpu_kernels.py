@@ -37,8 +37,18 @@ def test_rope_tables_vs_oracle(d, ax):
     assert np.max(np.abs(got[..., 1] - np.sin(phi))) <= 6e-8
 
 
-def _pack_case(dtype, d=128, heads=3):
-    w = I.custom("pack", 200, dtype, heads, d, [37, 64, 100], 10, prompt_rows=19)
+# (heads, rotary segment rows, prompt rows): a few ragged segments; then the
+# most segments one pack call takes, of sizes around the 64-row tile (empty,
+# single rows, 63/64/65, tiles shared by neighbouring segments), odd heads.
+PACK_CASES = {
+    "3seg": (3, [37, 64, 100], 19),
+    "16seg": (5, [1, 63, 64, 65, 0, 130, 7, 200, 64, 3, 1, 90, 40, 2, 127], 3),
+}
+
+
+def _pack_case(dtype, d=128, case="3seg"):
+    heads, rows, prompt = PACK_CASES[case]
+    w = I.custom("pack", 200, dtype, heads, d, rows, 10, prompt_rows=prompt)
     from streaming_video_diffusion_amd.stream import ChunkAttention
     ca = ChunkAttention(w)
     # one spare tile of capacity so rows past the padding can be checked
@@ -52,10 +62,11 @@ def _pack_case(dtype, d=128, heads=3):
     return w, ca
 
 
+@pytest.mark.parametrize("case", list(PACK_CASES))
 @pytest.mark.parametrize("d", [128, 64])
-def test_pack_bf16_layout_and_rotation(d):
-    note(f"[gpu] pack bf16 d={d}")
-    w, ca = _pack_case("bf16", d=d)
+def test_pack_bf16_layout_and_rotation(d, case):
+    note(f"[gpu] pack bf16 d={d} {case}")
+    w, ca = _pack_case("bf16", d=d, case=case)
     cap, H = ca.ctx.capacity_rows, w.heads
     kp = ca.ctx.k_data().view(H, cap, d)[:, :w.nk].permute(1, 0, 2).float().cpu().numpy().astype(np.float64)
     vp = unpack_v_bf16(ca.ctx.v_data(), H, d, cap, w.nk).float().cpu().numpy()
@@ -92,9 +103,10 @@ def test_pack_bf16_layout_and_rotation(d):
     assert torch.isnan(ca.ctx.k_data().view(H, cap, d)[:, pad_end:].float()).all()
 
 
-def test_pack_f32_layout_and_rotation():
-    note("[gpu] pack f32")
-    w, ca = _pack_case("f32")
+@pytest.mark.parametrize("case", list(PACK_CASES))
+def test_pack_f32_layout_and_rotation(case):
+    note(f"[gpu] pack f32 {case}")
+    w, ca = _pack_case("f32", case=case)
     cap, H, d = ca.ctx.capacity_rows, w.heads, w.head_dim
     pad_end = (w.nk + 63) // 64 * 64
     for buf in (ca.ctx.k_packed, ca.ctx.v_packed):
