@@ -81,8 +81,8 @@ def test_pack_bf16_layout_and_rotation(d, case):
         if rot_in_fwd:
             assert np.array_equal(got, k), f"{s.name}: keys must be stored unrotated"
             phi = np.zeros((s.rows, d // 2)) if pos is None else rope64.angles(pos, w.axis_dims, w.theta)
-            assert np.max(np.abs(tbl[row:row + s.rows, :, 0] - np.cos(phi))) <= 6e-8
-            assert np.max(np.abs(tbl[row:row + s.rows, :, 1] - np.sin(phi))) <= 6e-8
+            assert np.max(np.abs(tbl[row:row + s.rows, :, 0] - np.cos(phi)), initial=0.0) <= 6e-8
+            assert np.max(np.abs(tbl[row:row + s.rows, :, 1] - np.sin(phi)), initial=0.0) <= 6e-8
             assert np.array_equal(vp[row:row + s.rows], v), f"{s.name}: V must be copied bit-exactly"
             row += s.rows
             continue
@@ -118,7 +118,7 @@ def test_pack_f32_layout_and_rotation(case):
     row = 0
     for (k, v, pos), s in zip(segs, w.segments):
         ref = k.astype(np.float64) if pos is None else rope64.rotate(k, rope64.angles(pos, w.axis_dims, w.theta))
-        assert np.max(np.abs(kp[row:row + s.rows] - ref)) <= 2e-6, s.name
+        assert np.max(np.abs(kp[row:row + s.rows] - ref), initial=0.0) <= 2e-6, s.name
         assert np.array_equal(vp[row:row + s.rows], v)
         row += s.rows
 
