@@ -36,7 +36,7 @@ FWD_KERNEL = "fwd_bf16_kernel<128, 8, false, false> (balanced: tail halves + mai
 # 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written). Valid only for the
 # forward source these counters were taken on.
 TRAFFIC = {
-    "source_sha256": "0253973aa4e5dbdd8daa360bcd4995d4af3fe8361170545f2259529fb2579c77",
+    "source_sha256": "800b5b728a391f6ad97467864c11647de734773397c9d74798331f3a739224fe",
     "fetch_kib": 790504.8,
     "write_kib": 153447.6,
     "fetch_scale": 2.0,

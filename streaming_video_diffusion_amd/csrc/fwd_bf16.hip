@@ -5,7 +5,9 @@
 // deep-dive page, attention paragraph after the DiT configuration table;
 // the moving part of the window attends to the whole window: StreamRender-H3
 // page, streaming-context section). K arrives already rotated by the pack
-// step; the query rotation is fused into the Q load.
+// step (in the rotate-in-forward build it arrives unrotated and each tile is
+// rotated in LDS once it has landed); the query rotation is fused into the Q
+// load.
 //
 // Work decomposition: a workgroup of NW waves owns NW*32 query rows of one
 // head; each wave owns 32 queries, two waves share a SIMD.
@@ -27,13 +29,15 @@
 //     stores V transposed with a 16-row permutation so the A operand (V^T) is
 //     one 16-byte LDS read per lane;
 //   * K and V^T tiles of 64 keys stream through three LDS stages with direct
-//     global->LDS 16-byte loads (no staging registers), XOR-swizzled so the
+//     buffer->LDS 16-byte loads (no staging registers), XOR-swizzled so the
 //     operand reads are free of bank conflicts; the scores of tile kt+1 are
 //     formed while the softmax and P.V of tile kt run;
 //   * the workgroup -> (head, query tile) map keeps the workgroups that run
-//     together on one XCD on the same head, so its K/V tiles hit that XCD's L2.
-#include <type_traits>
-
+//     together on one XCD on the same head, so its K/V tiles hit that XCD's L2;
+//   * the same kernel serves split-KV (each workgroup one run of key tiles,
+//     storing its normalised partial output and natural log-sum-exp) and the
+//     balanced last round (its units as two key halves into a workspace,
+//     merged by tail_combine_kernel).
 #include "sa_internal.h"
 
 namespace sa {
