@@ -84,35 +84,41 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m streaming_video_diffusion_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        L.sa_make_rope_tables.argtypes = [ctypes.POINTER(RopeSpec), vp, i64, vp, vp]
-        L.sa_make_rope_tables.restype = i32
-        L.sa_packed_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
-        L.sa_packed_bytes.restype = i32
-        L.sa_pack_context.argtypes = [ctypes.POINTER(Context), ctypes.POINTER(Segment), i32, vp]
-        L.sa_pack_context.restype = i32
-        L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
-                                 ctypes.c_float, vp, i32, i64, i64, vp]
-        L.sa_forward.restype = i32
-        L.sa_forward_ws.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
-                                    ctypes.c_float, vp, i32, i64, i64, vp, ctypes.c_size_t, vp]
-        L.sa_forward_ws.restype = i32
-        L.sa_forward_workspace_bytes.argtypes = [ctypes.POINTER(Context), i64, ctypes.POINTER(ctypes.c_size_t)]
-        L.sa_forward_workspace_bytes.restype = i32
-        L.sa_forward_split.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
-                                       ctypes.c_float, i32, vp, vp, vp]
-        L.sa_forward_split.restype = i32
-        L.sa_combine_splits.argtypes = [i32, i64, i32, i32, vp, vp, vp, i32, i64, i64, vp]
-        L.sa_combine_splits.restype = i32
-        L.sa_status_string.argtypes = [i32]
-        L.sa_status_string.restype = ctypes.c_char_p
-        L.sa_last_error.argtypes = []
-        L.sa_last_error.restype = ctypes.c_char_p
-        L.sa_abi_version.argtypes = []
-        L.sa_abi_version.restype = i32
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path):
+    """A libstreamattn build at ``path`` with the ABI's signatures declared
+    (``lib()`` caches the default one)."""
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.sa_make_rope_tables.argtypes = [ctypes.POINTER(RopeSpec), vp, i64, vp, vp]
+    L.sa_make_rope_tables.restype = i32
+    L.sa_packed_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    L.sa_packed_bytes.restype = i32
+    L.sa_pack_context.argtypes = [ctypes.POINTER(Context), ctypes.POINTER(Segment), i32, vp]
+    L.sa_pack_context.restype = i32
+    L.sa_forward.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                             ctypes.c_float, vp, i32, i64, i64, vp]
+    L.sa_forward.restype = i32
+    L.sa_forward_ws.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                ctypes.c_float, vp, i32, i64, i64, vp, ctypes.c_size_t, vp]
+    L.sa_forward_ws.restype = i32
+    L.sa_forward_workspace_bytes.argtypes = [ctypes.POINTER(Context), i64, ctypes.POINTER(ctypes.c_size_t)]
+    L.sa_forward_workspace_bytes.restype = i32
+    L.sa_forward_split.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                   ctypes.c_float, i32, vp, vp, vp]
+    L.sa_forward_split.restype = i32
+    L.sa_combine_splits.argtypes = [i32, i64, i32, i32, vp, vp, vp, i32, i64, i64, vp]
+    L.sa_combine_splits.restype = i32
+    L.sa_status_string.argtypes = [i32]
+    L.sa_status_string.restype = ctypes.c_char_p
+    L.sa_last_error.argtypes = []
+    L.sa_last_error.restype = ctypes.c_char_p
+    L.sa_abi_version.argtypes = []
+    L.sa_abi_version.restype = i32
+    return L
 
 
 def _status_name(status):

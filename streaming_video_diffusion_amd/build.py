@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstreamattn.so")
+# the rotate-in-forward variant (keys rotated in the forward's key-tile load)
+ROTK_LIB = os.path.join(PKG, "libstreamattn_rotk.so")
+ROTK_FLAGS = ("-DSA_ROTATE_K_IN_FORWARD=1",)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -69,5 +72,5 @@ if __name__ == "__main__":
                     help="variant: keys rotated in the forward's key-tile load, not in the pack")
     ap.add_argument("--out", default=LIB, help="library path to write")
     args = ap.parse_args()
-    flags = ("-DSA_ROTATE_K_IN_FORWARD=1",) if args.rotate_k_in_forward else ()
+    flags = ROTK_FLAGS if args.rotate_k_in_forward else ()
     print(build(verbose=True, extra_flags=flags, lib_path=args.out))
