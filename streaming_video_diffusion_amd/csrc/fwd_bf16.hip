@@ -531,28 +531,40 @@ void fwd_bf16_kernel(FwdArgs a) {
     // next tile's scores is needed between tiles.
     f32x16 s[2], sb[2];
     if constexpr (ROTK) rotate_k(t_begin);
-    qk(buf_of(t_begin), s, zero16);
-    int kt = t_begin;
-    for (; kt + 1 < ntiles; kt += 2) {
-        if constexpr (ROTK) rotate_k(kt + 1);
-        issue(kt + 2);
-        mask(s, kt);
-        qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
-        end_tile();
-        if constexpr (ROTK) rotate_k(kt + 2);
-        issue(kt + 3);
-        mask(sb, kt + 1);
-        qk_exp_pv(buf_of(kt + 2), s, buf_of(kt + 1), sb);
-        end_tile();
-    }
-    if (kt < ntiles) {
-        // Last (odd) tile: the next-tile scores read a resident buffer and are
-        // discarded.
-        if constexpr (ROTK) rotate_k(kt + 1);
-        issue(kt + 2);
-        mask(s, kt);
-        qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
-        end_tile();
+    // A wave whose 32 query rows all lie past nq (the last query tile of a
+    // short call) computes nothing; it still issues its share of every tile
+    // load and meets every barrier, in the same order as the other waves.
+    const bool wave_has_rows = (int64_t)qt * BM + wu * 32 < a.nq;
+    if (wave_has_rows) {
+        qk(buf_of(t_begin), s, zero16);
+        int kt = t_begin;
+        for (; kt + 1 < ntiles; kt += 2) {
+            if constexpr (ROTK) rotate_k(kt + 1);
+            issue(kt + 2);
+            mask(s, kt);
+            qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
+            end_tile();
+            if constexpr (ROTK) rotate_k(kt + 2);
+            issue(kt + 3);
+            mask(sb, kt + 1);
+            qk_exp_pv(buf_of(kt + 2), s, buf_of(kt + 1), sb);
+            end_tile();
+        }
+        if (kt < ntiles) {
+            // Last (odd) tile: the next-tile scores read a resident buffer and
+            // are discarded.
+            if constexpr (ROTK) rotate_k(kt + 1);
+            issue(kt + 2);
+            mask(s, kt);
+            qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
+            end_tile();
+        }
+    } else {
+        for (int kt = t_begin; kt < ntiles; ++kt) {
+            if constexpr (ROTK) rotate_k(kt + 1);
+            issue(kt + 2);
+            end_tile();
+        }
     }
 
     // ---- per-row check and store ----------------------------------------------
