@@ -36,9 +36,9 @@ FWD_KERNEL = "fwd_bf16_kernel<128, 8, false, false> (balanced: tail halves + mai
 # 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written). Valid only for the
 # forward source these counters were taken on.
 TRAFFIC = {
-    "source_sha256": "800b5b728a391f6ad97467864c11647de734773397c9d74798331f3a739224fe",
-    "fetch_kib": 790504.8,
-    "write_kib": 153447.6,
+    "source_sha256": "23e5f617e509175344f8bcdc17c0c1d9e64b6abad26c7615f9e65b460e27ca81",
+    "fetch_kib": 994392.4,
+    "write_kib": 158672.8,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
