@@ -54,10 +54,12 @@ __device__ __forceinline__ void norm_row(float (&x)[E], const NormArgs &n, int h
 // averages the P x P full-resolution rows (f, P i + a, P j + b). One 16-byte
 // chunk (E elements) of K and of V, at element offsets koff / voff within a
 // row, is summed in float32 and scaled by 1/P^2.
-template <typename VT, int E, typename T>
+template <typename VT, int E, typename T, int PC = 0>
 __device__ __forceinline__ void pooled_chunk(const PackSeg &s, const T *ks, const T *vs, int64_t sr, int64_t koff,
                                              int64_t voff, float (&kx)[E], float (&vx)[E]) {
-    const int P = s.pool;
+    // PC > 0: the pooling factor known at compile time, so each block row's
+    // loads are all issued before the first is used
+    const int P = PC > 0 ? PC : s.pool;
     const int pw = s.grid_w / P;
     const int64_t cells = (int64_t)(s.grid_h / P) * pw;
     const int64_t f = sr / cells;
@@ -66,15 +68,34 @@ __device__ __forceinline__ void pooled_chunk(const PackSeg &s, const T *ks, cons
     const int64_t base = (f * s.grid_h + (int64_t)P * i) * s.grid_w + (int64_t)P * j;
 #pragma unroll
     for (int e = 0; e < E; ++e) kx[e] = vx[e] = 0.f;
-    for (int a = 0; a < P; ++a) {
-        for (int b = 0; b < P; ++b) {
-            const int64_t r = base + (int64_t)a * s.grid_w + b;
-            const VT kr = *reinterpret_cast<const VT *>(ks + r * s.k_rs + koff);
-            const VT vr = *reinterpret_cast<const VT *>(vs + r * s.v_rs + voff);
+    if constexpr (PC > 0) {
+        for (int a = 0; a < PC; ++a) {
+            VT kr[PC], vr[PC];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                kx[e] += (float)kr[e];
-                vx[e] += (float)vr[e];
+            for (int b = 0; b < PC; ++b) {
+                const int64_t r = base + (int64_t)a * s.grid_w + b;
+                kr[b] = *reinterpret_cast<const VT *>(ks + r * s.k_rs + koff);
+                vr[b] = *reinterpret_cast<const VT *>(vs + r * s.v_rs + voff);
+            }
+#pragma unroll
+            for (int b = 0; b < PC; ++b)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    kx[e] += (float)kr[b][e];
+                    vx[e] += (float)vr[b][e];
+                }
+        }
+    } else {
+        for (int a = 0; a < P; ++a) {
+            for (int b = 0; b < P; ++b) {
+                const int64_t r = base + (int64_t)a * s.grid_w + b;
+                const VT kr = *reinterpret_cast<const VT *>(ks + r * s.k_rs + koff);
+                const VT vr = *reinterpret_cast<const VT *>(vs + r * s.v_rs + voff);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    kx[e] += (float)kr[e];
+                    vx[e] += (float)vr[e];
+                }
             }
         }
     }
@@ -157,7 +178,13 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
         bf16x8 vv;
         if (s.pool > 1) {
             float vx[8];
-            pooled_chunk<bf16x8, 8>(s, ks, vs, sr, h * s.k_hs + chunk * 8, h * s.v_hs + chunk * 8, x, vx);
+            const int64_t ko = h * s.k_hs + chunk * 8, vo = h * s.v_hs + chunk * 8;
+            if (s.pool == 2)
+                pooled_chunk<bf16x8, 8, bf16, 2>(s, ks, vs, sr, ko, vo, x, vx);
+            else if (s.pool == 4)
+                pooled_chunk<bf16x8, 8, bf16, 4>(s, ks, vs, sr, ko, vo, x, vx);
+            else
+                pooled_chunk<bf16x8, 8>(s, ks, vs, sr, ko, vo, x, vx);
 #pragma unroll
             for (int e = 0; e < 8; ++e) vv[e] = (bf16)vx[e];
         } else {
