@@ -143,6 +143,41 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name, *, dtype=None, shape=None, device=None, contiguous=False):
+    """Raise ValueError unless tensor ``t`` has the given dtype, shape (None
+    entries match any size), device and, if asked, a contiguous layout. The
+    kernels index these buffers by the context's sizes, so a mismatch would
+    read or write outside them."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and a != w for a, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _expect_norm(norm, heads, head_dim, device, name):
+    if norm is None or norm.weight is None:
+        return
+    w = norm.weight
+    _expect(w, f"{name}.weight", dtype=torch.float32, device=device, contiguous=True)
+    if w.dim() == 1 and w.shape[0] != head_dim:
+        raise ValueError(f"{name}.weight has {w.shape[0]} elements, expected head_dim {head_dim}")
+    if w.dim() == 2 and tuple(w.shape) != (heads, head_dim):
+        raise ValueError(f"{name}.weight has shape {list(w.shape)}, expected [{heads}, {head_dim}]")
+
+
+def _expect_rows(t, name, ctx, rows=None):
+    """A [rows][heads][head_dim] view in the context's dtype, on its device."""
+    _expect(t, name, dtype=ctx.dtype, shape=(rows, ctx.heads, ctx.head_dim), device=ctx.device)
+
+
 def _rows_heads(t, name):
     if t.dim() == 3 and t.numel() == 0:
         return t.shape[1] * t.shape[2], t.shape[2]   # nothing is read: nominal dense strides
@@ -175,9 +210,11 @@ def padded_rows(rows):
 
 def sa_make_rope_tables(pos, head_dim, axis_dims, theta, table=None, stream=None):
     """Rotary table [n][head_dim/2][2] (cos, sin) of positions ``pos`` [n][3] f32."""
+    _expect(pos, "pos", dtype=torch.float32, shape=(None, 3), contiguous=True)
     n = pos.shape[0]
     if table is None:
         table = torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device=pos.device)
+    _expect(table, "table", dtype=torch.float32, shape=(n, head_dim // 2, 2), device=pos.device, contiguous=True)
     spec = RopeSpec(head_dim, (ctypes.c_int32 * 3)(*axis_dims), float(theta))
     _check("sa_make_rope_tables", lib().sa_make_rope_tables(ctypes.byref(spec), _ptr(pos), n, _ptr(table),
                                                             _stream(stream)))
@@ -194,6 +231,7 @@ class PackedContext:
         self.k_packed = torch.empty(n // elem, dtype=dtype, device=device)
         self.v_packed = torch.empty(n // elem, dtype=dtype, device=device)
         self.heads, self.head_dim, self.dtype = heads, head_dim, dtype
+        self.device = self.k_packed.device
         self.capacity_rows = cap
         self.rows = 0
 
@@ -239,10 +277,23 @@ def sa_pack_context(ctx, segments, stream=None, k_norm=None):
     ``(s, grid_h, grid_w)`` as in :func:`make_segment`."""
     keep = []
     segs = []
-    for seg in segments:
+    for i, seg in enumerate(segments):
         k, v, dst, rope = seg[:4]
         norm = seg[4] if len(seg) > 4 else k_norm
         pool = seg[5] if len(seg) > 5 else None
+        _expect_rows(k, f"segment {i} k", ctx)
+        _expect_rows(v, f"segment {i} v", ctx, rows=k.shape[0])
+        _expect_norm(norm, ctx.heads, ctx.head_dim, ctx.device, f"segment {i} k_norm")
+        if rope is not None:
+            rows = k.shape[0]
+            if pool is not None:
+                s_, gh, gw = (int(x) for x in pool)
+                if s_ >= 1 and gh > 0 and gw > 0 and gh % s_ == 0 and gw % s_ == 0:
+                    rows = rows // (gh * gw) * (gh // s_) * (gw // s_)
+            _expect(rope, f"segment {i} rope", dtype=torch.float32, shape=(None, ctx.head_dim // 2, 2),
+                    device=ctx.device, contiguous=True)
+            if rope.shape[0] < rows:
+                raise ValueError(f"segment {i} rope has {rope.shape[0]} rows, the segment packs {rows}")
         n = None if norm is None else norm.struct()
         keep.append(n)
         segs.append(make_segment(k, v, dst, rope, n, pool))
@@ -252,14 +303,30 @@ def sa_pack_context(ctx, segments, stream=None, k_norm=None):
     del keep
 
 
+def _check_query(ctx, q, q_rope, q_norm):
+    _expect_rows(q, "q", ctx)
+    if q_rope is not None:
+        _expect(q_rope, "q_rope", dtype=torch.float32, shape=(q.shape[0], ctx.head_dim // 2, 2), device=ctx.device,
+                contiguous=True)
+    _expect_norm(q_norm, ctx.heads, ctx.head_dim, ctx.device, "q_norm")
+
+
+def _check_out(ctx, q, out):
+    _expect(out, "out", shape=(q.shape[0], ctx.heads, ctx.head_dim), device=ctx.device)
+    if out.dtype not in _DTYPES:
+        raise ValueError(f"out has dtype {out.dtype}, expected torch.bfloat16 or torch.float32")
+
+
 def sa_forward(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None, q_norm=None):
     """Attention of ``q`` [Nq][heads][head_dim] over the packed context;
     ``q_norm`` (a ``Norm``) normalises every query row before its rotation."""
+    _check_query(ctx, q, q_rope, q_norm)
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:
         softmax_scale = ctx.head_dim ** -0.5
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _check_out(ctx, q, out)
     ors, ohs = _rows_heads(out, "out")
     c = ctx.struct()
     qn = None if q_norm is None else q_norm.struct()
@@ -283,11 +350,15 @@ def sa_forward_ws(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=N
     """``sa_forward`` with a device workspace (a tensor of at least
     ``sa_forward_workspace_bytes`` bytes, or None) that balances the last
     round of workgroups."""
+    _check_query(ctx, q, q_rope, q_norm)
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:
         softmax_scale = ctx.head_dim ** -0.5
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _check_out(ctx, q, out)
+    if workspace is not None:
+        _expect(workspace, "workspace", device=ctx.device, contiguous=True)
     ors, ohs = _rows_heads(out, "out")
     c = ctx.struct()
     qn = None if q_norm is None else q_norm.struct()
@@ -304,6 +375,7 @@ def sa_forward_split(ctx, q, n_splits, q_rope=None, softmax_scale=None, partial=
     """Split-KV attention: per key run, the normalised partial output float32
     [n_splits][Nq][heads][head_dim] and the natural log-sum-exp float32
     [n_splits][Nq][heads]. Returns (partial, lse)."""
+    _check_query(ctx, q, q_rope, q_norm)
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:
         softmax_scale = ctx.head_dim ** -0.5
@@ -312,6 +384,9 @@ def sa_forward_split(ctx, q, n_splits, q_rope=None, softmax_scale=None, partial=
         partial = torch.empty((n_splits, nq, ctx.heads, ctx.head_dim), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((n_splits, nq, ctx.heads), dtype=torch.float32, device=q.device)
+    _expect(partial, "partial", dtype=torch.float32, shape=(n_splits, nq, ctx.heads, ctx.head_dim), device=ctx.device,
+            contiguous=True)
+    _expect(lse, "lse", dtype=torch.float32, shape=(n_splits, nq, ctx.heads), device=ctx.device, contiguous=True)
     c = ctx.struct()
     qn = None if q_norm is None else q_norm.struct()
     _check("sa_forward_split", lib().sa_forward_split(ctypes.byref(c), _ptr(q), nq, qrs, qhs, _ptr(q_rope),
@@ -322,9 +397,14 @@ def sa_forward_split(ctx, q, n_splits, q_rope=None, softmax_scale=None, partial=
 
 def sa_combine_splits(partial, lse, out=None, out_dtype=torch.bfloat16, stream=None):
     """Merge split-KV results into [Nq][heads][head_dim] (LSE-weighted mean)."""
+    _expect(partial, "partial", dtype=torch.float32, shape=(None, None, None, None), contiguous=True)
     n_splits, nq, heads, d = partial.shape
+    _expect(lse, "lse", dtype=torch.float32, shape=(n_splits, nq, heads), device=partial.device, contiguous=True)
     if out is None:
         out = torch.empty((nq, heads, d), dtype=out_dtype, device=partial.device)
+    _expect(out, "out", shape=(nq, heads, d), device=partial.device)
+    if out.dtype not in _DTYPES:
+        raise ValueError(f"out has dtype {out.dtype}, expected torch.bfloat16 or torch.float32")
     ors, ohs = _rows_heads(out, "out")
     _check("sa_combine_splits", lib().sa_combine_splits(n_splits, nq, heads, d, _ptr(partial), _ptr(lse), _ptr(out),
                                                         _DTYPES[out.dtype], ors, ohs, _stream(stream)))
