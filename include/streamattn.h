@@ -72,7 +72,15 @@ typedef int32_t sa_status;
 #define SA_ERR_UNSUPPORTED (-6) /* valid but not implemented (e.g. head_dim other than 64 / 128) */
 #define SA_ERR_HIP (-7)         /* a HIP launch failed; sa_last_error() holds HIP's message */
 
+/* Element type. A 32-bit enumeration in C and in C++ alike; C++ fixes the
+ * underlying type so that any 32-bit value a caller passes is a value of the
+ * type, which the library then validates (no undefined load of an
+ * out-of-range enumerator). */
+#ifdef __cplusplus
+typedef enum : int32_t { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+#else
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+#endif
 
 /*
  * Rotary specification. The head dimension is cut into three consecutive
@@ -205,6 +213,10 @@ typedef struct {
 
 /*
  * sa_packed_bytes -- size in bytes of each of k_packed and v_packed.
+ * The packed buffers are the persistent per-layer K/V buffers kept in the
+ * layout the attention kernel reads, allocated once by the caller and
+ * reused for every chunk (StreamRender-H3 page, inference-acceleration
+ * section).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED,
  * SA_ERR_CAPACITY (capacity_rows not a multiple of SA_ROW_ALIGN, or one head's
  * packed K/V not below 2^31 bytes).
@@ -214,6 +226,15 @@ sa_status sa_packed_bytes(int32_t heads, int32_t head_dim, sa_dtype dtype, int64
 
 /*
  * sa_pack_context -- gather segments into the packed K/V buffers.
+ *
+ * Defined by: the prefix key/values (conditions, reference, sink) computed
+ * once per denoising step and reused while only recent history and the
+ * current chunk are recomputed (StreamRender-H3 page, streaming-context
+ * section); one persistent K/V buffer per layer and step bank, in the
+ * kernel's layout, whose dynamic region is rewritten in place
+ * (StreamRender-H3 page, inference-acceleration section); the style-prompt
+ * key/values kept in every self-attention layer and older history held at
+ * coarser resolution (AlayaRenderer-Flash page, key contributions).
  *
  * Each segment's rows are written to packed rows [dst_row, dst_row + rows),
  * keys RMS-normalised when the segment has a k_norm and rotated by the
@@ -265,6 +286,11 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
  * sa_forward_ws -- sa_forward with a caller workspace that lets the bf16
  * forward balance its last round of workgroups.
  *
+ * The operation is sa_forward's (same passages); the workspace only changes
+ * how the work is spread over the chip, in the spirit of the pages' attention
+ * kernel tuned to the streaming shapes (StreamRender-H3 page,
+ * inference-acceleration section).
+ *
  * The bf16 forward runs one workgroup per (head, 256-query tile) unit and one
  * workgroup per compute unit at a time, so W units take ceil(W / n_cu)
  * rounds. When the last round would be at most half full (1920 units on 256
@@ -285,7 +311,8 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
- * sa_forward_workspace_bytes -- bytes of workspace sa_forward_ws uses for this
+ * sa_forward_workspace_bytes -- (see sa_forward_ws for the passages it
+ * serves) bytes of workspace sa_forward_ws uses for this
  * context and nq on the current device (0 when it would run as sa_forward):
  * 2 r * 256 * (head_dim + 1) * 4 for the r balanced units, at most
  * n_cu * 256 * (head_dim + 1) * 4 (33.8 MB at head_dim 128 on 256 CUs).
@@ -297,6 +324,13 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
  * sa_forward_split -- split-KV form of sa_forward for problems with few query
  * rows (the 40 audio-only queries of a joint chunk, or one GPU's head shard),
  * where one workgroup per (query tile, head) cannot fill the chip.
+ *
+ * Defined by: audio latents at 40 Hz attending jointly with the video tokens
+ * (MiniMax-H3 deep-dive page, components table and DiT paragraph); the pages'
+ * kernel picks its key-split count by the per-GPU work of the streaming
+ * shapes, which is small after head sharding (StreamRender-H3 page,
+ * inference-acceleration section). The run results combine by the
+ * log-sum-exp identity below.
  *
  * The packed keys are cut into n_splits runs of whole 64-key tiles, run s
  * covering tiles [floor(s T / n_splits), floor((s+1) T / n_splits)) of the
@@ -318,7 +352,9 @@ sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int
                            int32_t n_splits, float *partial, float *lse, hipStream_t stream);
 
 /*
- * sa_combine_splits -- merge sa_forward_split results:
+ * sa_combine_splits -- merge sa_forward_split results (the passages of
+ * sa_forward_split; the merge is the exact log-sum-exp identity of softmax
+ * over a union of disjoint key sets):
  *   out[r][h] = sum_s w_s partial[s][r][h] / sum_s w_s,  w_s = exp(lse[s][r][h] - max_s lse[s][r][h]).
  * out: device [nq][heads][head_dim] of out_dtype with the given element strides.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_UNSUPPORTED (head_dim),

@@ -19,6 +19,11 @@ LIB = os.path.join(PKG, "libstreamattn.so")
 # the rotate-in-forward variant (keys rotated in the forward's key-tile load)
 ROTK_LIB = os.path.join(PKG, "libstreamattn_rotk.so")
 ROTK_FLAGS = ("-DSA_ROTATE_K_IN_FORWARD=1",)
+# the host-sanitizer build: host code (argument validation, dispatch) with
+# AddressSanitizer and UndefinedBehaviorSanitizer; device code as usual
+SAN_LIB = os.path.join(PKG, "libstreamattn_san.so")
+SAN_FLAGS = tuple("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                  "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer -g".split())
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -70,7 +75,13 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--rotate-k-in-forward", action="store_true",
                     help="variant: keys rotated in the forward's key-tile load, not in the pack")
-    ap.add_argument("--out", default=LIB, help="library path to write")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="variant: host code with address and undefined-behaviour sanitizers")
+    ap.add_argument("--out", default=None, help="library path to write")
     args = ap.parse_args()
     flags = ROTK_FLAGS if args.rotate_k_in_forward else ()
-    print(build(verbose=True, extra_flags=flags, lib_path=args.out))
+    out = args.out or LIB
+    if args.sanitize:
+        flags = flags + SAN_FLAGS
+        out = args.out or SAN_LIB
+    print(build(verbose=True, extra_flags=flags, lib_path=out))
