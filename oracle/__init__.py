@@ -14,6 +14,8 @@ What it computes is the plain definition of the operation, in float64:
   applied before the rotation.
 * ``pool64``  -- s x s spatial mean pooling of aged history frames into a
   coarser tier (of keys before their normalisation and rotation, and of values).
+* ``tiers64`` -- which chunk feeds which history tier as chunks age (full
+  resolution -> 2x2 -> 4x4 -> dropped) and the fixed position template.
 * ``attn64``  -- dense softmax attention of the current chunk's queries over the
   concatenated key/value context (prompt KV | reference frame | history tiers |
   current chunk), vectorised with numpy per head and query block.
@@ -33,6 +35,6 @@ invariants, a library routine (SDPA) and brute force; nothing is "parity
 unpinned".
 """
 
-from . import rope64, norm64, pool64, attn64, brute  # noqa: F401
+from . import rope64, norm64, pool64, attn64, brute, tiers64  # noqa: F401
 
-__all__ = ["rope64", "norm64", "pool64", "attn64", "brute"]
+__all__ = ["rope64", "norm64", "pool64", "attn64", "brute", "tiers64"]

@@ -20,7 +20,7 @@ import math
 import numpy as np
 import torch
 
-from oracle import attn64, brute, norm64, pool64, rope64
+from oracle import attn64, brute, norm64, pool64, rope64, tiers64
 
 AX128 = (32, 48, 48)
 THETA = 10000.0
@@ -425,9 +425,72 @@ def pin_pooled_tier_attention():
     _close(got, ref, 1e-12, "pooled tier attention")
 
 
+def pin_tier_schedule():
+    """The reading of the three history tiers (AlayaRenderer-Flash page, key
+    contributions): while chunk c is generated the context holds chunk c-1 at
+    full resolution, c-2 at 2x2 and c-3 at 4x4, nothing older, and tiers stay
+    empty until their chunk exists."""
+    want = {0: (None, None, None), 1: (None, None, 0), 2: (None, 0, 1), 3: (0, 1, 2), 4: (1, 2, 3), 9: (6, 7, 8)}
+    for c, ages in want.items():
+        got = {n: j for n, _, j in tiers64.tier_chunks(c)}
+        assert (got["pool4"], got["pool2"], got["prev"]) == ages, (c, got)
+    assert [(n, s) for n, s, _ in tiers64.TIERS] == [("pool4", 4), ("pool2", 2), ("prev", 1)]
+    assert tiers64.template_t(3) == {"pool4": [1, 2, 3], "pool2": [4, 5, 6], "prev": [7, 8, 9],
+                                     "current": [10, 11, 12]}
+
+
+def pin_tier_ageing():
+    """One chunk's data moves down the tiers from one step to the next: the
+    4x4 tier at chunk c is the 2x2 pooling of the 2x2 tier at chunk c-1, and
+    the 2x2 tier at chunk c the 2x2 pooling of the full-resolution tier at
+    chunk c-1; the template positions do not move."""
+    rng = _rng(141)
+    frames, gh, gw = 2, 8, 4
+    data = {j: (rng.standard_normal((frames * gh * gw, 2, 4)), rng.standard_normal((frames * gh * gw, 2, 4)))
+            for j in range(6)}
+    seg = {c: tiers64.history_segments(lambda j: data[j], c, frames, gh, gw) for c in range(6)}
+    assert [len(seg[c]) for c in range(6)] == [0, 1, 2, 3, 3, 3]
+    for c in (4, 5):
+        (k4, v4, p4), (k2, v2, p2), (k1, v1, p1) = seg[c]
+        (_, _, q4), (pk2, pv2, q2), (pk1, pv1, q1) = seg[c - 1]
+        _close(k4, pool64.pool_frames(pk2, gh // 2, gw // 2, 2), 1e-14, "4x4 tier = 2x2 of last 2x2 tier (k)")
+        _close(v4, pool64.pool_frames(pv2, gh // 2, gw // 2, 2), 1e-14, "4x4 tier = 2x2 of last 2x2 tier (v)")
+        _close(k2, pool64.pool_frames(pk1, gh, gw, 2), 1e-14, "2x2 tier = 2x2 of last full tier (k)")
+        _close(v1, data[c - 1][1], 0.0, "full tier = previous chunk")
+        for a, b in ((p4, q4), (p2, q2), (p1, q1)):
+            _close(a, b, 0.0, "template positions")
+    assert seg[5][0][0].shape[0] == frames * (gh // 4) * (gw // 4)
+
+
+def pin_tier_attention_brute():
+    """Chunk 3's attention over prompt, reference, the three tiers and itself
+    == brute force over hand-pooled tiers at hand-written positions."""
+    rng = _rng(142)
+    d, ax, frames, gh, gw = 8, (2, 2, 4), 1, 4, 4
+    data = {j: (rng.standard_normal((gh * gw, 1, d)), rng.standard_normal((gh * gw, 1, d))) for j in range(4)}
+    prompt = (rng.standard_normal((3, 1, d)), rng.standard_normal((3, 1, d)), None)
+    ref_pos = np.array([[0.0, i, j] for i in range(gh) for j in range(gw)])
+    ref = (rng.standard_normal((gh * gw, 1, d)), rng.standard_normal((gh * gw, 1, d)), ref_pos)
+    q = rng.standard_normal((5, 1, d))
+    qp = np.array([[4.0, i, j] for i in range(gh) for j in range(gw)])[[0, 3, 6, 9, 15]]
+    got = tiers64.chunk_attention(q, qp, [prompt, ref], lambda j: data[j], 3, frames, gh, gw, ax, THETA, 0.4)
+
+    def cells(t, s):
+        return np.array([[t, s * i + (s - 1) / 2.0, s * j + (s - 1) / 2.0]
+                         for i in range(gh // s) for j in range(gw // s)])
+
+    hand = [prompt, ref,
+            (_pool_loops(data[0][0], gh, gw, 4), _pool_loops(data[0][1], gh, gw, 4), cells(1, 4)),
+            (_pool_loops(data[1][0], gh, gw, 2), _pool_loops(data[1][1], gh, gw, 2), cells(2, 2)),
+            (data[2][0], data[2][1], cells(3, 1)),
+            (data[3][0], data[3][1], cells(4, 1))]
+    want = brute.chunk_attention(q, qp, hand, ax, THETA, 0.4)
+    _close(got, want, 1e-12, "tiered chunk attention")
+
+
 ALL_PINS = [pin_brute_force, pin_rotation_closed_form, pin_rotation_group, pin_single_pair_scores,
             pin_softmax_rows, pin_constant_v, pin_joint_permutation, pin_zero_angle_is_sdpa,
             pin_two_keys, pin_degenerate, pin_translation, pin_row_selection, pin_rmsnorm_closed_form,
             pin_rmsnorm_invariants, pin_brute_force_qknorm, pin_qknorm_then_rotation, pin_split_lse_closed_forms,
             pin_split_merge_identity, pin_pool_brute_force, pin_pool_closed_forms, pin_pool_invariants,
-            pin_pooled_tier_attention]
+            pin_pooled_tier_attention, pin_tier_schedule, pin_tier_ageing, pin_tier_attention_brute]

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle_pins
-from oracle import attn64, norm64, pool64, rope64
+from oracle import attn64, norm64, pool64, rope64, tiers64
 
 
 def _rotate_with(fn):
@@ -145,6 +145,18 @@ def _split_with(lse_form, normalise=True):
     return split_attention
 
 
+def _template_reversed(frames):
+    names = [n for n, _, _ in tiers64.TIERS][::-1] + ["current"]
+    return {n: list(range(1 + i * frames, 1 + (i + 1) * frames)) for i, n in enumerate(names)}
+
+
+def _cell_corner(t_values, grid_h, grid_w, s):
+    gh, gw = grid_h // s, grid_w // s
+    hh, ww = np.meshgrid(np.arange(gh) * s, np.arange(gw) * s, indexing="ij")
+    return np.concatenate([np.stack([np.full(gh * gw, float(t)), hh.reshape(-1), ww.reshape(-1)], axis=1)
+                           for t in t_values], axis=0)
+
+
 MUTATIONS = {
     "pool_sum_not_mean": [(pool64, "pool_frames", _pool_with(lambda b: b.sum(axis=(2, 4))))],
     "pool_first_cell_only": [(pool64, "pool_frames", _pool_with(lambda b: b[:, :, 0, :, 0]))],
@@ -175,6 +187,13 @@ MUTATIONS = {
     "weights_times_keys": [(attn64, "attention", _attention_with(lambda k, v: k))],
     "scale_dropped": [(attn64, "attention", _attention_with(lambda k, v: v, use_scale=False))],
     "keys_not_rotated": [(attn64, "rotated_keys", _rotated_keys_unrotated)],
+    # history tiers: ages swapped, one step late, the current chunk fed back as history,
+    # the template's tier order reversed, a pooled cell at its corner instead of its centre
+    "tier_ages_swapped": [(tiers64, "TIERS", (("pool4", 4, 2), ("pool2", 2, 3), ("prev", 1, 1)))],
+    "tier_ages_late": [(tiers64, "TIERS", (("pool4", 4, 4), ("pool2", 2, 3), ("prev", 1, 2)))],
+    "tier_prev_is_current": [(tiers64, "TIERS", (("pool4", 4, 3), ("pool2", 2, 2), ("prev", 1, 0)))],
+    "tier_template_reversed": [(tiers64, "template_t", _template_reversed)],
+    "tier_cell_corner": [(tiers64, "cell_positions", _cell_corner)],
 }
 
 
