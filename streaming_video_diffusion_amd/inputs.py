@@ -286,6 +286,83 @@ def prefix_self_1344x768():
 VARIANTS = {w().name: w for w in (history_query_1344x768, first_window_1344x768, prefix_self_1344x768)}
 
 
+@dataclass
+class TierStream:
+    """Inputs of a chunk-by-chunk stream whose history ages through coarser
+    tiers: a style prompt and a reference frame fixed for the session, and
+    every chunk's queries, keys and values (``frames`` latent frames of
+    ``grid_h`` x ``grid_w`` tokens), drawn per chunk index. Positions come
+    from one fixed template: reference at t = 0, then ``slots`` history slots
+    of ``frames`` frames each (oldest first), then the current chunk; a slot
+    pooled s x s places each cell at the centre of the cells it covers. Which
+    chunk fills which slot is the stream's business, not this class's.
+    """
+    name: str
+    cfg_id: int
+    dtype: str
+    heads: int
+    head_dim: int
+    grid_h: int
+    grid_w: int
+    frames: int
+    prompt: int
+    slots: int = 3
+    theta: float = ROPE_THETA
+    axis_dims: tuple = None
+    scale: float = None
+    description: str = ""
+
+    def __post_init__(self):
+        if self.axis_dims is None:
+            self.axis_dims = AXIS_DIMS[self.head_dim]
+        if self.scale is None:
+            self.scale = 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def chunk_rows(self):
+        return self.frames * self.grid_h * self.grid_w
+
+    def _draw(self, chunk, tensor_id, rows):
+        # chunk -1 is the session's static part; seed words must be non-negative
+        rng = np.random.default_rng(np.random.SeedSequence([ENTROPY, self.cfg_id, chunk + 1, tensor_id]))
+        x = rng.standard_normal((rows, self.heads, self.head_dim), dtype=np.float32)
+        return round_bf16(x) if self.dtype == "bf16" else x
+
+    def static_kv(self):
+        """``[(k, v, pos_or_None)]`` of the prompt (no rotary) and the reference frame (t = 0)."""
+        ref_rows = self.grid_h * self.grid_w
+        return [(self._draw(-1, 1, self.prompt), self._draw(-1, 2, self.prompt), None),
+                (self._draw(-1, 3, ref_rows), self._draw(-1, 4, ref_rows),
+                 frame_positions([0], self.grid_h, self.grid_w))]
+
+    def chunk_q(self, c):
+        return self._draw(c, 0, self.chunk_rows)
+
+    def chunk_kv(self, c):
+        """Full-resolution keys and values of chunk ``c``."""
+        return self._draw(c, 1, self.chunk_rows), self._draw(c, 2, self.chunk_rows)
+
+    def slot_t(self, slot):
+        """Frame indices of history slot ``slot`` (0 = oldest); ``slot = slots`` is the current chunk."""
+        return list(range(1 + slot * self.frames, 1 + (slot + 1) * self.frames))
+
+    def slot_positions(self, slot, pool=1):
+        return frame_positions(self.slot_t(slot), self.grid_h, self.grid_w, pool)
+
+
+def tier_stream_small(dtype="bf16", head_dim=128):
+    """A small tiered stream: 16 x 12 grid, 3 frames per chunk, 3 heads."""
+    return TierStream(f"tier_stream_small_{dtype}_d{head_dim}", 20 + head_dim // 64 + (dtype == "f32") * 4, dtype, 3,
+                      head_dim, 12, 16, 3, 40, description="tiered history stream, 16x12 grid, 3 frames per chunk")
+
+
+def tier_stream_1344x768():
+    """The 1344x768 tiered stream (84 x 48 grid, 3 latent frames per chunk, 40 heads, d 128): at steady state
+    12096 queries over 256 + 4032 + 756 + 3024 + 12096 + 12096 = 32260 keys."""
+    return TierStream("tier_stream_1344x768", 30, "bf16", 40, 128, 48, 84, 3, 256,
+                      description="1344x768 tiered history stream: 12096 q x up to 32260 kv, 40 heads, d128")
+
+
 def custom(name, cfg_id, dtype, heads, head_dim, seg_rows, nq, rotary=True, prompt_rows=0,
            pos_scale=40.0, axis_dims=None, theta=ROPE_THETA, scale=None, qk_norm=None):
     """Arbitrary-shape workload for tests: random positions, given row counts.

@@ -14,6 +14,8 @@ Device memory comes from torch; every step of the computation runs in the
 library's HIP kernels.
 """
 
+import collections
+
 import numpy as np
 import torch
 
@@ -124,3 +126,106 @@ class ChunkAttention:
         if weights is None:
             return None, None
         return (weights[0], self.w.norm_eps), (weights[1], self.w.norm_eps)
+
+
+class TierStreamAttention:
+    """One layer's attention over a stream of chunks whose history ages
+    through three tiers by temporal distance (AlayaRenderer-Flash page, key
+    contributions and technical details): while chunk c is generated the
+    context holds, after the static prompt and reference frame, chunk c-3 as
+    4x4 spatial means, chunk c-2 as 2x2 means, chunk c-1 at full resolution
+    and chunk c itself; older chunks leave the context, and a tier stays
+    empty until its chunk exists.
+
+    The stream keeps the raw (not yet normalised or rotated) keys and values
+    of the last four chunks -- the tensors the caller passes to ``step`` --
+    and every step rewrites the packed context's dynamic region in place
+    from them: the pack forms each tier's means from its chunk's
+    full-resolution rows, normalises and rotates every key at its template
+    position and writes it after the static rows, which are never touched
+    again. The position template is fixed (reference at t = 0, the tiers
+    oldest first, then the current chunk), so its rotary tables are built
+    once.
+
+    ``stream`` is an ``inputs.TierStream`` (shapes, template positions,
+    static prompt / reference values).
+    """
+
+    # (pooling factor, age in chunks) of the history tiers, oldest first
+    TIERS = ((4, 3), (2, 2), (1, 1))
+
+    def __init__(self, stream, device="cuda", out_dtype=None):
+        st = stream
+        self.st = st
+        dev = torch.device(device)
+        self.device = dev
+        self.dtype = torch.bfloat16 if st.dtype == "bf16" else torch.float32
+        self.out_dtype = out_dtype or self.dtype
+        rows = st.chunk_rows
+        self.static = []
+        row = 0
+        for k, v, pos in st.static_kv():
+            table = None
+            if pos is not None:
+                table = B.sa_make_rope_tables(torch.from_numpy(pos).to(dev), st.head_dim, st.axis_dims, st.theta)
+            self.static.append((torch.from_numpy(k).to(dev).to(self.dtype), torch.from_numpy(v).to(dev).to(self.dtype),
+                                row, table))
+            row += k.shape[0]
+        self.static_rows = row
+        # rotary tables of the template: one per history slot at its pooling factor, and the current chunk's
+        self.tier_tables = []
+        for slot, (s, _) in enumerate(self.TIERS):
+            pos = torch.from_numpy(st.slot_positions(slot, s)).to(dev)
+            self.tier_tables.append(B.sa_make_rope_tables(pos, st.head_dim, st.axis_dims, st.theta))
+        cur = torch.from_numpy(st.slot_positions(len(self.TIERS))).to(dev)
+        self.q_table = B.sa_make_rope_tables(cur, st.head_dim, st.axis_dims, st.theta)
+        cap = self.static_rows + sum(rows // (s * s) for s, _ in self.TIERS) + rows
+        self.ctx = B.PackedContext(st.heads, st.head_dim, self.dtype, cap, device=dev)
+        self.ctx.rows = self.static_rows
+        self.history = collections.deque(maxlen=len(self.TIERS) + 1)  # (k, v) of chunks c-3 .. c
+        self.chunk = -1
+        self.out = torch.empty((rows, st.heads, st.head_dim), dtype=self.out_dtype, device=dev)
+        self.workspace = None
+
+    def pack_static(self, stream=None):
+        """Pack the prompt and the reference frame (once per session and bank)."""
+        self.ctx.rows = max(self.ctx.rows, self.static_rows)
+        B.sa_pack_context(self.ctx, [(k, v, dst, table) for k, v, dst, table in self.static], stream=stream)
+
+    def tiers(self):
+        """``[(pool, chunk index, k, v)]`` of the history of the current
+        chunk, oldest first; empty tiers are left out."""
+        c = self.chunk
+        out = []
+        for s, age in self.TIERS:
+            j = c - age
+            if j >= 0:
+                k, v = self.history[len(self.history) - 1 - age]
+                out.append((s, j, k, v))
+        return out
+
+    def step(self, q, k, v, stream=None):
+        """Generate the next chunk: ``q``, ``k``, ``v`` are its queries and
+        raw keys / values, ``[chunk_rows][heads][head_dim]`` device tensors
+        the stream keeps (by reference) while the chunk is in the context.
+        Rewrites the dynamic region and runs the forward; returns the output."""
+        st = self.st
+        self.history.append((k, v))
+        self.chunk += 1
+        segs = []
+        row = self.static_rows
+        for s, _, tk, tv in self.tiers():
+            slot = [t for t, _ in self.TIERS].index(s)
+            pool = (s, st.grid_h, st.grid_w) if s > 1 else None
+            segs.append((tk, tv, row, self.tier_tables[slot], None, pool))
+            row += tk.shape[0] // (s * s)
+        segs.append((k, v, row, self.q_table))
+        row += k.shape[0]
+        self.ctx.rows = row
+        B.sa_pack_context(self.ctx, segs, stream=stream)
+        ws = B.sa_forward_workspace_bytes(self.ctx, q.shape[0])
+        if ws and (self.workspace is None or self.workspace.numel() < ws):
+            self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        B.sa_forward_ws(self.ctx, q, self.q_table, st.scale, out=self.out, stream=stream,
+                        workspace=self.workspace if ws else None)
+        return self.out

@@ -93,3 +93,24 @@ def test_pooled_positions_are_cell_means():
         full = I.frame_positions([1, 2], 48, 84)
         pooled = I.frame_positions([1, 2], 48, 84, pool=s)
         np.testing.assert_array_equal(pooled, pool64.pool_frames(full[:, None, :], 48, 84, s)[:, 0, :])
+
+
+def test_tier_stream_draws_and_template():
+    from oracle import tiers64
+    st = I.tier_stream_small()
+    (pk, pv, ppos), (rk, rv, rpos) = st.static_kv()
+    assert pk.shape == (40, 3, 128) and ppos is None
+    assert rk.shape == (12 * 16, 3, 128) and np.all(rpos[:, 0] == 0)
+    assert np.array_equal(st.chunk_q(2), st.chunk_q(2))
+    draws = [st.chunk_q(0), *st.chunk_kv(0), *st.chunk_kv(1), pk, pv, rk[:40], rv[:40]]
+    for i in range(len(draws)):
+        for j in range(i + 1, len(draws)):
+            n = min(len(draws[i]), len(draws[j]))
+            assert not np.array_equal(draws[i][:n], draws[j][:n])
+    assert np.all(st.chunk_q(0) == I.round_bf16(st.chunk_q(0)))
+    tt = tiers64.template_t(st.frames)
+    for slot, name in enumerate(["pool4", "pool2", "prev", "current"]):
+        assert st.slot_t(slot) == tt[name]
+    for slot, (name, s, _) in enumerate(tiers64.TIERS):
+        want = tiers64.cell_positions(tt[name], st.grid_h, st.grid_w, s)
+        np.testing.assert_array_equal(st.slot_positions(slot, s), want.astype(np.float32))
