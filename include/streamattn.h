@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 
 /* Packed context capacity (rows) must be a multiple of this (one key tile). */
 #define SA_ROW_ALIGN 64
@@ -61,6 +61,10 @@ extern "C" {
 #define SA_MAX_SPLITS 256
 /* Largest spatial pooling factor of a segment (sa_segment.pool). */
 #define SA_MAX_POOL 8
+/* Bytes of device scratch sa_forward_noalloc holds on each device it runs on
+ * (64 MiB: the balanced last round needs at most 50.7 MB at head_dim 128 on
+ * 256 compute units). */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef int32_t sa_status;
 #define SA_OK 0
@@ -309,6 +313,29 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
                         int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
                         void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sa_forward_noalloc -- sa_forward_ws for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It computes exactly what sa_forward_ws computes with a
+ * large enough workspace (same kernels, same launches), but the balanced last
+ * round's scratch is a device array the library holds, SA_NOALLOC_SCRATCH_BYTES
+ * on every device it runs on, from that device's first call until the process
+ * ends. The call itself allocates nothing; the caller passes inputs and
+ * output as for sa_forward.
+ * Every call on one device shares that device's scratch, and a call leaves
+ * its partial results there: calls that may overlap on one device (other
+ * streams, other threads, replays of graphs holding it) race and must be
+ * ordered by the caller. No call relies on what an earlier one left.
+ * Other arguments, result and errors as sa_forward; SA_ERR_CAPACITY when the
+ * forward needs more scratch than SA_NOALLOC_SCRATCH_BYTES (nothing is
+ * launched), SA_ERR_UNSUPPORTED on a device index of 64 or more, SA_ERR_HIP
+ * when the scratch's device address cannot be obtained.
+ */
+sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                             int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                             void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride,
+                             hipStream_t stream);
 
 /*
  * sa_forward_workspace_bytes -- (see sa_forward_ws for the passages it

@@ -21,6 +21,7 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_ROW_ALIGN = 64
 SA_MAX_SEGMENTS = 16
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20  # device scratch sa_forward_noalloc holds per device
 SA_MAX_SPLITS = 256
 
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
@@ -105,6 +106,10 @@ def load(path):
     L.sa_forward_ws.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
                                 ctypes.c_float, vp, i32, i64, i64, vp, ctypes.c_size_t, vp]
     L.sa_forward_ws.restype = i32
+    if hasattr(L, "sa_forward_noalloc"):  # ABI version 5 on
+        L.sa_forward_noalloc.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
+                                         ctypes.c_float, vp, i32, i64, i64, vp]
+        L.sa_forward_noalloc.restype = i32
     L.sa_forward_workspace_bytes.argtypes = [ctypes.POINTER(Context), i64, ctypes.POINTER(ctypes.c_size_t)]
     L.sa_forward_workspace_bytes.restype = i32
     L.sa_forward_split.argtypes = [ctypes.POINTER(Context), vp, i64, i64, i64, vp, ctypes.POINTER(RmsNorm),
@@ -367,6 +372,25 @@ def sa_forward_ws(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=N
                                                 None if qn is None else ctypes.byref(qn), float(softmax_scale),
                                                 _ptr(out), _DTYPES[out.dtype], ors, ohs, ws, ws_bytes,
                                                 _stream(stream)))
+    return out
+
+
+def sa_forward_noalloc(ctx, q, out, q_rope=None, softmax_scale=None, stream=None, q_norm=None):
+    """``sa_forward_ws``'s result with the library's own per-device scratch
+    instead of a workspace: the call allocates nothing (``out`` is required).
+    Calls that overlap on one device share that scratch and race."""
+    _check_query(ctx, q, q_rope, q_norm)
+    qrs, qhs = _rows_heads(q, "q")
+    if softmax_scale is None:
+        softmax_scale = ctx.head_dim ** -0.5
+    _check_out(ctx, q, out)
+    ors, ohs = _rows_heads(out, "out")
+    c = ctx.struct()
+    qn = None if q_norm is None else q_norm.struct()
+    _check("sa_forward_noalloc", lib().sa_forward_noalloc(ctypes.byref(c), _ptr(q), q.shape[0], qrs, qhs,
+                                                          _ptr(q_rope), None if qn is None else ctypes.byref(qn),
+                                                          float(softmax_scale), _ptr(out), _DTYPES[out.dtype], ors,
+                                                          ohs, _stream(stream)))
     return out
 
 

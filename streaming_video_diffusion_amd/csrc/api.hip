@@ -8,8 +8,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sa_internal.h"
+
+// Scratch of sa_forward_noalloc: the balanced last round's float32 partial
+// outputs and log-sum-exps. Each device the library runs on holds its own copy
+// until the process ends. In host code this name is only a stand-in: kernels
+// and copies take the device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -365,21 +372,11 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
     return SA_OK;
 }
 
-sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
-                        const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
-                        sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
-    g_err[0] = 0;
-    sa::FwdArgs a;
-    sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
-                                    out_dtype, o_row_stride, o_head_stride, a);
-    if (st != SA_OK || nq == 0) return st;
-    const TailPlan p = tail_plan(ctx, nq);
-    if (!p.units || !workspace) return forward_launch(ctx, a, stream);
-    const size_t need = tail_bytes(p.units, ctx->head_dim);
-    if (workspace_bytes < need)
-        return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
-    if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+// The three launches of a balanced forward (a: validated arguments, p: a plan
+// with units > 0, workspace: device memory of at least tail_bytes(p.units)).
+static sa_status balanced_launch(const sa_context *ctx, const sa::FwdArgs &a, const TailPlan &p, void *workspace,
+                                 hipStream_t stream) {
+    const int64_t nq = a.nq;
     const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
     float *part = static_cast<float *>(workspace);
     float *lse = part + (size_t)p.units * 2 * bm * ctx->head_dim;
@@ -396,19 +393,85 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
     sa::TailCombineArgs c{};  // ... and the merge of the halves.
     c.part = part;
     c.lse = lse;
-    c.out = out;
+    c.out = a.out;
     c.nq = nq;
-    c.o_rs = o_row_stride;
-    c.o_hs = o_head_stride;
+    c.o_rs = a.o_rs;
+    c.o_hs = a.o_hs;
     c.heads = ctx->heads;
     c.n_qt = (int)((nq + bm - 1) / bm);
     c.bm = (int)bm;
     c.first_unit = p.first_unit;
     c.units = p.units;
-    c.out_f32 = out_dtype == SA_F32;
+    c.out_f32 = a.out_f32;
     e = sa::launch_tail_combine(c, ctx->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "tail merge launch");
     return SA_OK;
+}
+
+sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride, int64_t q_head_stride,
+                        const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale, void *out,
+                        sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
+                                    out_dtype, o_row_stride, o_head_stride, a);
+    if (st != SA_OK || nq == 0) return st;
+    const TailPlan p = tail_plan(ctx, nq);
+    if (!p.units || !workspace) return forward_launch(ctx, a, stream);
+    const size_t need = tail_bytes(p.units, ctx->head_dim);
+    if (workspace_bytes < need)
+        return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return balanced_launch(ctx, a, p, workspace, stream);
+}
+
+// Device address of `scratch` per device, looked up once per device (with
+// that device current) on the first sa_forward_noalloc there.
+static constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[kMaxScratchDevices];
+
+static sa_status scratch_address(void **addr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(SA_ERR_UNSUPPORTED, "device %d: sa_forward_noalloc serves devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, 256)) return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) gave an unaligned address");
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return SA_OK;
+}
+
+sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
+                             int64_t q_head_stride, const float *q_rope, const sa_rmsnorm *q_norm, float softmax_scale,
+                             void *out, sa_dtype out_dtype, int64_t o_row_stride, int64_t o_head_stride,
+                             hipStream_t stream) {
+    g_err[0] = 0;
+    sa::FwdArgs a;
+    sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
+                                    out_dtype, o_row_stride, o_head_stride, a);
+    if (st != SA_OK || nq == 0) return st;
+    const TailPlan p = tail_plan(ctx, nq);
+    if (!p.units) return forward_launch(ctx, a, stream);
+    const size_t need = tail_bytes(p.units, ctx->head_dim);
+    if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+        return fail(SA_ERR_CAPACITY, "this forward needs %zu bytes of scratch; sa_forward_noalloc holds %zu",
+                    need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SA_OK) return st;
+    // Every word of the scratch a call reads is written earlier in the same
+    // call (the key halves, then the merge), so nothing needs clearing.
+    return balanced_launch(ctx, a, p, ws, stream);
 }
 
 sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,

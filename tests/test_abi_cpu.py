@@ -50,12 +50,12 @@ def test_header_constants_match_binding():
     assert ctypes.sizeof(B.Segment) == 96
     assert ctypes.sizeof(B.Context) == 48
     assert ctypes.sizeof(B.RmsNorm) == 16
-    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 4
+    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 5
     assert int(re.search(r"#define SA_MAX_POOL (\d+)", text).group(1)) == 8
 
 
 def test_version_and_status_strings(L):
-    assert L.sa_abi_version() == 4
+    assert L.sa_abi_version() == 5
     assert L.sa_status_string(0) == b"SA_OK"
     for name, val in ERR.items():
         assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
@@ -229,6 +229,27 @@ def test_forward_ws_errors(L):
     assert ws(ctx(), out=FAKE + 2) == ERR["ALIGN"]
     assert ws(ctx(), q=None) == ERR["NULL"]
     assert ws(ctx(), nq=0) == 0
+
+
+def test_forward_noalloc_errors(L):
+    def na(c, q=FAKE, nq=8, out=FAKE * 3, odt=B.SA_BF16, ors=256, qn=None):
+        return L.sa_forward_noalloc(None if c is None else ctypes.byref(c), q, nq, 256, 128, None,
+                                    None if qn is None else ctypes.byref(qn), 0.1, out, odt, ors, 128, None)
+    assert na(None) == ERR["NULL"]
+    assert na(ctx(rows=0)) == ERR["CAPACITY"]
+    assert na(ctx(), odt=9) == ERR["DTYPE"]
+    assert na(ctx(), out=None) == ERR["NULL"]
+    assert na(ctx(), out=FAKE + 2) == ERR["ALIGN"]
+    assert na(ctx(), q=None) == ERR["NULL"]
+    assert na(ctx(), qn=norm(eps=-0.5)) == ERR["SHAPE"]
+    assert na(ctx(), nq=0) == 0
+    assert L.sa_last_error() == b""
+
+
+def test_noalloc_scratch_limit_declared():
+    text = open(HEADER).read()
+    m = re.search(r"#define SA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.SA_NOALLOC_SCRATCH_BYTES
 
 
 def test_forward_split_errors(L):
