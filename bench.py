@@ -27,21 +27,40 @@ METRIC = "attention TFLOP/s + ms/chunk at 1344x768 (12096 q x 28480 kv, 40 heads
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (published)
 FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf16.hip")
-FWD_KERNEL = "fwd_bf16_kernel<128, 8, false, false> (balanced: tail halves + main grid) + tail_combine_kernel<128, false>"
-# HBM traffic of one forward at 1344x768 (its three dispatches: the forward
-# kernel over the balanced tail's key halves, over the other units, and the
-# merge), from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB, summed over the
-# three; profiles/fwd_bf16_1344x768_hbm_traffic.txt), each scaled by what the
-# same counter reads for a plain device copy of known size (FETCH_SIZE counts
-# 0.5x the bytes read, WRITE_SIZE 1.0x the bytes written). Valid only for the
-# forward source these counters were taken on.
+# HBM traffic of one forward at 1344x768, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per forward; profiles/fwd_bf16_1344x768_hbm_traffic.txt),
+# each scaled by what the same counter reads for a plain device copy of known
+# size (FETCH_SIZE counts 0.5x the bytes read, WRITE_SIZE 1.0x the bytes
+# written). Valid only for the forward source these counters were taken on
+# (None: not taken on the current source).
 TRAFFIC = {
-    "source_sha256": "23e5f617e509175344f8bcdc17c0c1d9e64b6abad26c7615f9e65b460e27ca81",
-    "fetch_kib": 994341.9,
-    "write_kib": 159035.5,
+    "source_sha256": "91a05cb5cd06bc3ae3823d7f27f9ffff96e91fcffb77af555a1bd656dd3fb1ac",
+    "fetch_kib": 467209.2,
+    "write_kib": 120962.1,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
+
+
+def bf16_rows_per_workgroup():
+    """Query rows per workgroup of the bf16 forward, read off the workspace
+    the library asks for: n_cu + 1 heads of one query row leave one unit in a
+    second round, whose two key halves take 2 * rows * (d + 1) * 4 bytes."""
+    import torch
+    from streaming_video_diffusion_amd import binding as B
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx = B.PackedContext(n_cu + 1, 128, torch.bfloat16, 128, device="cuda")
+    ctx.rows = 128
+    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * 129 * 4)
+
+
+def fwd_kernel_name(ca):
+    bm = bf16_rows_per_workgroup()
+    units = -(-ca.w.nq // bm) * ca.w.heads
+    if ca.workspace is not None:
+        return (f"fwd_bf16_kernel<128, false, false> ({units} units of {bm} queries, the last round's as key "
+                f"halves) + tail_combine_kernel<128, false>")
+    return f"fwd_bf16_kernel<128, false, false> ({units} workgroups of {bm} queries)"
 
 
 def parse():
@@ -151,7 +170,7 @@ def shard_measure(steps):
     ms = a.elapsed_time(b) / steps
     return {"heads": 5, "nq": w.nq, "nk": w.nk, "forward_ms": ms,
             "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12,
-            "workgroups": ((w.nq + 255) // 256) * w.heads}
+            "workgroups": -(-w.nq // bf16_rows_per_workgroup()) * w.heads}
 
 
 def _time(fn, stream, steps):
@@ -207,7 +226,43 @@ def other_workloads(steps, skip):
             res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps)}
         del ca
         torch.cuda.empty_cache()
+    res["tier_stream_1344x768"] = tier_stream_measure(steps)
     return res
+
+
+def tier_stream_measure(steps):
+    """Per-chunk cost of the ageing history at 1344x768 in steady state (all
+    three tiers present: 32260 keys): the in-place repack of the dynamic
+    region from the raw K/V of the last four chunks (pooling the two older
+    tiers again), then the forward."""
+    import torch
+    from streaming_video_diffusion_amd import inputs as I
+    from streaming_video_diffusion_amd.stream import TierStreamAttention
+    st = I.tier_stream_1344x768()
+    stream = torch.cuda.current_stream()
+    dt = torch.bfloat16
+    chunks = []
+    for c in range(5):
+        k, v = st.chunk_kv(c)
+        chunks.append(tuple(torch.from_numpy(x).to("cuda:0").to(dt) for x in (st.chunk_q(c), k, v)))
+    ts = TierStreamAttention(st, device="cuda:0")
+    ts.pack_static(stream)
+    for c in range(4):
+        ts.step(*chunks[c], stream=stream)
+    i = [4]
+
+    def age():
+        q, k, v = chunks[i[0] % 5]
+        ts.age(k, v, stream)
+        i[0] += 1
+
+    age_ms = _time(age, stream, steps)
+    q = chunks[(i[0] - 1) % 5][0]
+    fwd_ms = _time(lambda: ts.forward(q, stream), stream, steps)
+    step_ms = _time(lambda: (age(), ts.forward(chunks[(i[0] - 1) % 5][0], stream)), stream, steps)
+    w_flops = 4.0 * st.chunk_rows * ts.ctx.rows * st.head_dim * st.heads
+    return {"nq": st.chunk_rows, "nk": int(ts.ctx.rows), "age_repack_ms": age_ms, "forward_ms": fwd_ms,
+            "step_ms": step_ms, "tflops_step": w_flops / (step_ms * 1e-3) / 1e12}
 
 
 class SclkSampler:
@@ -350,7 +405,7 @@ def main():
         "sclk": sclk.summary(),
         "roofline": {
             "bound": "mfma" if bf16 else "alu",
-            "kernel": FWD_KERNEL if bf16 else "fwd_f32_kernel",
+            "kernel": fwd_kernel_name(calls[0]) if bf16 else "fwd_f32_kernel",
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",

@@ -295,10 +295,10 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
  * kernel tuned to the streaming shapes (StreamRender-H3 page,
  * inference-acceleration section).
  *
- * The bf16 forward runs one workgroup per (head, 256-query tile) unit and one
+ * The bf16 forward runs one workgroup per (head, 384-query tile) unit and one
  * workgroup per compute unit at a time, so W units take ceil(W / n_cu)
- * rounds. When the last round would be at most half full (1920 units on 256
- * CUs: 7.5 rounds run as 8), its r units are computed first as 2r key halves
+ * rounds. When the last round would be at most half full (e.g. 1040 units on
+ * 256 CUs: 4.06 rounds run as 5), its r units are computed first as 2r key halves
  * (half a round) into the workspace, the other W - r units as usual, and the
  * halves merged by their log-sum-exps (the identity sa_forward_split rests
  * on): the same result as sa_forward up to rounding, in fewer rounds.
@@ -341,8 +341,8 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
  * sa_forward_workspace_bytes -- (see sa_forward_ws for the passages it
  * serves) bytes of workspace sa_forward_ws uses for this
  * context and nq on the current device (0 when it would run as sa_forward):
- * 2 r * 256 * (head_dim + 1) * 4 for the r balanced units, at most
- * n_cu * 256 * (head_dim + 1) * 4 (33.8 MB at head_dim 128 on 256 CUs).
+ * 2 r * 384 * (head_dim + 1) * 4 for the r balanced units, at most
+ * n_cu * 384 * (head_dim + 1) * 4 (50.7 MB at head_dim 128 on 256 CUs).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, and the context checks of sa_forward.
  */
 sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes);

@@ -9,11 +9,14 @@
 // rotated in LDS once it has landed); the query rotation is fused into the Q
 // load.
 //
-// Work decomposition: a workgroup of NW waves owns NW*32 query rows of one
-// head; each wave owns 32 queries, two waves share a SIMD.
+// Work decomposition: a workgroup of four waves, one per SIMD, owns 384 query
+// rows of one head; each wave owns three blocks of 32 queries, so every K or
+// V^T operand it reads from LDS feeds three matrix-core products.
 //   * Q is RMS-normalised when asked (QK-norm) and rotated in fp32,
 //     multiplied by scale*log2(e), rounded once to bf16 and kept in registers
-//     as the B operand of v_mfma_f32_32x32x16_bf16;
+//     for the whole kernel as the B operand of v_mfma_f32_32x32x16_bf16 (two
+//     blocks in AGPRs, the third in VGPRs: the output accumulators, 192 AGPRs
+//     at head_dim 128, fill the rest of the AGPR file);
 //   * scores are formed transposed, S^T = K Q^T (A = K tile from LDS), so the
 //     32x32 accumulator puts one query column in each lane: a row max is an
 //     in-lane reduction plus one exchange between half-waves, and the row sum
@@ -21,17 +24,20 @@
 //   * the main pass holds the softmax anchor at 0 (P = 2^s, log2 units) for
 //     the whole row with no per-tile max: exact as long as nothing over- or
 //     underflows, which one check per row at the end establishes; rows that
-//     fail it (rare) are recomputed by a second pass that tracks the running
-//     max explicitly;
+//     fail it (rare) are recomputed by a second pass that first finds the exact
+//     row max, then forms P = 2^(s - max);
 //   * P^T is rounded to bf16 and is already in the B-operand layout of
-//     O^T += V^T P^T; the row sum accumulates those same bf16 values with
-//     v_dot2 (numerator and denominator see identical weights). The pack step
-//     stores V transposed with a 16-row permutation so the A operand (V^T) is
-//     one 16-byte LDS read per lane;
+//     O^T += V^T P^T; the row sum adds the float32 values P was rounded from.
+//     The pack step stores V transposed with a 16-row permutation so the A
+//     operand (V^T) is one 16-byte LDS read per lane;
+//   * the hot loop is a software pipeline over 32-key units: one stage issues
+//     the P.V products of unit i, the Q.K^T products of unit i + 2 and the
+//     exponentials of unit i + 1, one matrix-core op per slot with that slot's
+//     operand reads and VALU work after it, in an order the compiler may not
+//     change (sched_barrier);
 //   * K and V^T tiles of 64 keys stream through three LDS stages with direct
 //     buffer->LDS 16-byte loads (no staging registers), XOR-swizzled so the
-//     operand reads are free of bank conflicts; the scores of tile kt+1 are
-//     formed while the softmax and P.V of tile kt run;
+//     operand reads are free of bank conflicts, one barrier per tile;
 //   * the workgroup -> (head, query tile) map keeps the workgroups that run
 //     together on one XCD on the same head, so its K/V tiles hit that XCD's L2;
 //   * the same kernel serves split-KV (each workgroup one run of key tiles,
@@ -40,51 +46,41 @@
 //     merged by tail_combine_kernel).
 #include "sa_internal.h"
 
+#include <type_traits>
+
 namespace sa {
 
 namespace {
 
-constexpr int BN = 64;                // keys per tile
-constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int BN = 64;   // keys per tile
+constexpr int kNW = 4;   // waves per workgroup, one per SIMD
+constexpr int kQB = 3;   // 32-query blocks per wave
+constexpr int kBM = kNW * kQB * 32;  // queries per workgroup
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
-// 16-byte operand read at an LDS byte address.
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
     return *reinterpret_cast<lds_bf16x8 *>((uintptr_t)addr);
 }
 
-// Physical 16-byte chunk of a tile row: XOR swizzles that keep the matrix-core
-// operand reads (32 rows, one logical chunk) free of LDS bank conflicts for
-// 32 or 64 banks. A 256-byte row swizzles by its low 4 row bits; a 128-byte
-// row (two rows per 64 banks) by ((r >> 1) & 7) ^ ((r & 1) << 2).
 __device__ __forceinline__ int swz256(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz128(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
 
 template <int D, int NW>
 struct Tile {
-    static constexpr int KROW = D * 2;          // bytes per K row
-    static constexpr int VROW = BN * 2;         // bytes per V^T row (128)
+    static constexpr int KROW = D * 2;
+    static constexpr int VROW = BN * 2;
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = D * VROW;
-    static constexpr int BUF = KBYTES + VBYTES;  // bytes per buffer
-    static constexpr int KINSTR = KBYTES / 1024;  // 1 KiB per wave-wide direct load
+    static constexpr int BUF = KBYTES + VBYTES;
+    static constexpr int KINSTR = KBYTES / 1024;
     static constexpr int VINSTR = VBYTES / 1024;
     static constexpr int KROWS_PER_INSTR = 1024 / KROW;
     static constexpr int VROWS_PER_INSTR = 1024 / VROW;
     static_assert(KINSTR % NW == 0 && VINSTR % NW == 0, "tile loads must split evenly over the waves");
 
     __device__ static __forceinline__ int kswz(int r, int c) { return D == 128 ? swz256(r, c) : swz128(r, c); }
-
-    // Operand-read addresses. For a lane reading row r (K) or d-row r (V^T),
-    // the physical chunk is (logical chunk) ^ key(r) with key depending only
-    // on r mod 16, and the XORed bits (5..7) are disjoint from the row and
-    // buffer bits. So every read address of a tile is a per-lane base plus
-    // the buffer offset, XORed with a constant, plus an immediate offset:
-    //   K   row 32 tt + l32, chunk 2 j + hf:  ((A0 + buf) ^ 32 j) + tt * 32 * KROW
-    //   V^T row 32 c + l32,  chunk 4 tt + 2 g + hf:  ((B0 + buf) ^ (64 tt + 32 g)) + c * 32 * VROW
-    // A0 and B0 are the only per-lane address registers kept live.
     __device__ static __forceinline__ uint32_t kbase(int l32, int hf) {
         const int key = D == 128 ? (l32 & 15) : swz128(l32, 0);
         return (uint32_t)(l32 * KROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
@@ -93,14 +89,8 @@ struct Tile {
         const int key = swz128(l32, 0);
         return (uint32_t)(KBYTES + l32 * VROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
     }
-    // byte offset of logical chunk c of K row r / V^T row r inside a buffer
     __device__ static __forceinline__ int koff(int r, int c) { return r * KROW + kswz(r, c) * 16; }
-    __device__ static __forceinline__ int voff(int r, int c) { return KBYTES + r * VROW + swz128(r, c) * 16; }
 
-    // Loop-invariant per-lane byte offsets of this wave's share of one tile's
-    // direct global->LDS loads (K relative to the tile's first K row, V^T
-    // relative to the tile's first V^T column), so each tile only moves a
-    // wave-uniform base pointer.
     struct Plan {
         uint32_t k[KINSTR / NW];
         uint32_t v[VINSTR / NW];
@@ -121,16 +111,6 @@ struct Tile {
         }
         return pl;
     }
-
-    // Issue this wave's share of the direct buffer->LDS loads of one K/V^T
-    // tile: the loop-invariant lane offsets plus the tile's wave-uniform byte
-    // offset (a scalar operand). kr / vr describe one head's packed K / V^T
-    // (below 2^31 bytes each). The packed capacity is a multiple of the tile,
-    // so the last tile never leaves the allocation; its rows past nk hold
-    // zeros written by the pack step, and their scores are masked. (Buffer
-    // rather than global loads: with a global load to LDS in flight the
-    // compiler can only wait for all LDS reads at once, which would undo the
-    // read-ahead of the operand reads.)
     __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, __amdgpu_buffer_rsrc_t kr,
                                                  __amdgpu_buffer_rsrc_t vr, uint32_t k0, int w) {
 #pragma unroll
@@ -142,41 +122,102 @@ struct Tile {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024),
                                                      16, (int)pl.v[ii], (int)(k0 * 2), 0, 0);
     }
-
 };
 
 __device__ __forceinline__ void vm_lgkm_cnt0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
-// Value of lane l ^ 32 (the other half-wave holds the same query column).
 __device__ __forceinline__ float half_swap_partner(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    // r[0]: lanes 32..63 took lanes 0..31; r[1]: lanes 0..31 took lanes 32..63
     return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
 }
 
-template <int D, int NW, bool OUT_F32, bool ROTK>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool B>
+using bconst = std::integral_constant<bool, B>;
+
+// The products are written as inline assembly so that each operand sits in the
+// register file chosen for it: O^T accumulators and Q in AGPRs, scores, P and
+// the LDS operands in VGPRs. The compiler does not track matrix-core latency
+// through inline assembly, so every read of a product's result by other
+// instructions goes through one of the wait-state helpers below, which take
+// the registers they protect as operands.
+
+// With G the product is preceded by two wait states of its own: where
+// register pressure makes the compiler move accumulators into place right
+// before a product (the rotate-in-forward build), a VALU write needs those two
+// wait states before a product may read the register.
+
+// O^T += V^T P^T (accumulator in AGPRs; a = V^T, b = P^T).
+template <bool G>
+__device__ __forceinline__ void mfma_pv(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (G) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// S^T = K Q^T (first k-step) and S^T += K Q^T (scores in VGPRs, a = K, b = Q in AGPRs).
+template <bool G>
+__device__ __forceinline__ void mfma_qk0(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (G) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+template <bool G>
+__device__ __forceinline__ void mfma_qk(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (G) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// the same with Q in VGPRs (the query block that does not fit the AGPR file)
+template <bool G>
+__device__ __forceinline__ void mfma_qk0_v(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (G) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+template <bool G>
+__device__ __forceinline__ void mfma_qk_v(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (G) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Scores just formed: wait until the products writing them have finished
+// (an 8-pass product needs 11 wait states before other instructions touch its
+// result; four s_nop 7 give 32).
+__device__ __forceinline__ void drain_s(f32x16 (&s)[kQB]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]));
+}
+// Output accumulators: wait until the last products writing them have finished.
+template <int DT>
+__device__ __forceinline__ void drain_o(f32x16 (&o)[kQB][DT]) {
+    if constexpr (DT == 4)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
+                       "+a"(o[1][2]), "+a"(o[1][3]), "+a"(o[2][0]), "+a"(o[2][1]), "+a"(o[2][2]), "+a"(o[2][3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[2][0]), "+a"(o[2][1]));
+}
+// P just written by VALU instructions: wait states before a product reads it.
+__device__ __forceinline__ void valu_to_mfma(bf16x8 (&p)[kQB][2]) {
+    asm volatile("s_nop 4" : "+v"(p[0][0]), "+v"(p[0][1]), "+v"(p[1][0]), "+v"(p[1][1]), "+v"(p[2][0]), "+v"(p[2][1]));
+}
+
+template <int D, bool OUT_F32, bool ROTK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int BM = NW * 32;  // queries per workgroup (32 per wave)
-    constexpr int DC = D / 16;   // k-steps of Q.K^T
-    constexpr int DT = D / 32;   // 32-row d tiles of O^T
-    constexpr int NSTAGE = 3;    // tiles resident or in flight in LDS
+    constexpr int QB = kQB;           // 32-query blocks per wave
+    constexpr int NW = kNW;           // waves, one per SIMD
+    constexpr int QA = 2;             // query blocks whose Q lives in AGPRs
+    constexpr int BM = kBM;           // queries per workgroup
+    constexpr int DC = D / 16;        // k-steps of Q.K^T
+    constexpr int DT = D / 32;        // 32-row d tiles of O^T
+    constexpr int NSTAGE = 3;         // LDS buffers; a tile is loaded NSTAGE - 1 tiles ahead
+    constexpr int NVR = 2 * DT;       // V^T operand reads per 32-key unit
     typedef Tile<D, NW> T;
     extern __shared__ __align__(1024) unsigned char smem[];
 
-    // XCD-aware workgroup -> (head, query tile) map: consecutive dispatch ids
-    // go round-robin over the 8 XCDs; give each XCD a contiguous logical range.
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
     const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
     const int n_qt = (int)((a.nq + BM - 1) / BM);
-    // logical = (head * n_splits + split) * n_qt + query tile: the workgroups
-    // of one head and key range are neighbours, so they share an XCD's L2.
-    // In a balanced-tail launch, logical = 2 * unit + half instead, unit
-    // counting from the first of the last tail_units (head, query tile) units.
     int qt, head, split, n_splits = a.n_splits, tail_unit = 0;
     if (a.tail_units) {
         tail_unit = logical >> 1;
@@ -198,19 +239,20 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int lane = t & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
-    const int64_t q_row = (int64_t)qt * BM + w * 32 + l32;
+    // query row of block b of this lane
+    const int64_t row0 = (int64_t)qt * BM + w * (QB * 32) + l32;
 
     // ---- Q load: rotate in fp32, scale by scale*log2(e), one bf16 rounding ----
-    bf16x8 qreg[DC];
-    {
+    bf16x8 qreg[QB][DC];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int64_t q_row = row0 + 32 * b;
         const bool valid = q_row < a.nq;
         const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + q_row * a.q_rs + (int64_t)head * a.q_hs;
-        const float *tb = a.q_rope ? a.q_rope + q_row * D : nullptr;  // [row][D/2][2]
+        const float *tb = a.q_rope ? a.q_rope + q_row * D : nullptr;
         bf16x8 qraw[DC];
 #pragma unroll
         for (int j = 0; j < DC; ++j) qraw[j] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * j + 8 * hf) : bf16x8{};
-        // QK-norm: the row's mean square over both half-waves' elements, in
-        // float32, before the rotation.
         float qs = 1.0f;
         const float *qw = nullptr;
         if (a.q_norm.on) {
@@ -251,17 +293,22 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = (bf16)(xf[e] * a.scale_log2);
             }
-            qreg[j] = x;
+            // Q stays in AGPRs for the whole kernel (the B operand of S^T = K Q^T),
+            // except the blocks the AGPR file has no room for.
+            if (b < QA) asm volatile("" : "=a"(qreg[b][j]) : "0"(x));
+            else qreg[b][j] = x;
         }
     }
 
-    f32x16 o[DT];
+    f32x16 o[QB][DT];
 #pragma unroll
-    for (int c = 0; c < DT; ++c) o[c] = f32x16{};
-    float l = 0.f;
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int c = 0; c < DT; ++c) o[b][c] = f32x16{};
+    float l[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) l[b] = 0.f;
 
-    // Buffer descriptors of this head's packed K and V^T (raw, byte-addressed,
-    // 32-bit data format word as the CDNA buffer instructions expect).
     const int head_bytes = (int)(a.cap * D * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<unsigned char *>(const_cast<void *>(a.k)) + (int64_t)head * a.cap * D * 2, 0, head_bytes,
@@ -271,51 +318,30 @@ void fwd_bf16_kernel(FwdArgs a) {
         0x00020000);
     const int ntiles_all = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
-    // This workgroup's key tiles [t_begin, ntiles) (all of them without split-KV).
     const int t_begin = split_first_tile(split, n_splits, ntiles_all);
     const int ntiles = split_first_tile(split + 1, n_splits, ntiles_all);
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    const f32x16 zero16 = f32x16{};
-    // Per-lane operand-read bases as LDS byte addresses. smem is 1024-byte
-    // aligned and every buffer starts at a multiple of 32 KiB, so the XOR
-    // swizzle (bits 5..7) commutes with adding either.
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
     const uint32_t A0 = T::kbase(l32, hf) + lds0;
     const uint32_t B0 = T::vbase(l32, hf) + lds0;
 
-    // Every tile follows one schedule on every path: at tile kt a wave issues
-    // its share of tile kt+2's direct loads, computes, waits for its own loads
-    // (vmcnt 0) and meets one workgroup barrier. So at each barrier every
-    // wave's share of the tile two ahead has landed, and a buffer is refilled
-    // only after every wave has passed the barrier that ends its last use.
     auto buf_of = [&](int kt) __attribute__((always_inline)) { return smem + (kt % NSTAGE) * T::BUF; };
-    // The lane offsets are recomputed at every issue from an opaque copy of
-    // the lane id: a few VALU ops instead of per-lane 64-bit pointers kept
-    // live across the loop, and the loads keep the SGPR-base form.
     auto issue = [&](int kt) __attribute__((always_inline)) {
         if (kt < ntiles) T::issue(buf_of(kt), T::plan(a.cap, wu, lane), krs, vrs, (uint32_t)(kt * BN), wu);
     };
-    // Every LDS read of the tile has returned (lgkmcnt 0) and every load this
-    // wave issued has landed (vmcnt 0) before the barrier, so a buffer is
-    // reloaded only after every wave is done with it.
+    // End of a tile: this wave's loads (of the tile after next) have landed and
+    // every LDS read has returned; then the workgroup barrier.
     auto end_tile = [&]() __attribute__((always_inline)) {
         vm_lgkm_cnt0();
         __syncthreads();
     };
-
-    // Rotate-in-forward (ROTK): the keys of tile kt sit unrotated in its LDS
-    // buffer; the workgroup rotates them in place from the per-row tables
-    // (one bf16 rounding), then meets a barrier that waits for LDS only, so
-    // the tile loads in flight keep going. Its table loads are issued before
-    // the next tile loads, so waiting for them never waits for those.
     auto rotate_k = [&](int kt_r) __attribute__((always_inline)) {
         if (kt_r < ntiles) {
-            unsigned char *b = buf_of(kt_r);
+            unsigned char *bb = buf_of(kt_r);
             const float *tbl = a.k_table + (int64_t)kt_r * BN * D;
 #pragma unroll
             for (int i = t; i < BN * (D / 8); i += NW * 64) {
                 const int r = i / (D / 8), c = i % (D / 8);
-                bf16x8 *p = reinterpret_cast<bf16x8 *>(b + T::koff(r, c));
+                bf16x8 *p = reinterpret_cast<bf16x8 *>(bb + T::koff(r, c));
                 const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tbl + (r * (D / 2) + 4 * c) * 2);
                 const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tbl + (r * (D / 2) + 4 * c) * 2 + 4);
                 const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
@@ -330,150 +356,191 @@ void fwd_bf16_kernel(FwdArgs a) {
                 *p = y;
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
 
-    // S^T (log2 units) minus the seed: K Q^T + seed, for the tile in buf.
-    auto qk = [&](const unsigned char *buf, f32x16 (&s)[2], const f32x16 &seed) __attribute__((always_inline)) {
-        const uint32_t kb0 = (uint32_t)(buf - smem) + A0;
-        auto kread = [&](int j, int tt) __attribute__((always_inline)) {
-            return lds_read16((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW);
-        };
-#pragma unroll
-        for (int j = 0; j < DC; ++j) {
-            const bf16x8 ka0 = kread(j, 0), ka1 = kread(j, 1);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[j], j ? s[0] : seed, 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[j], j ? s[1] : seed, 0, 0, 0);
-        }
+    // LDS byte address bases of 32-key unit (kt, half): K rows 32 half .. of
+    // tile kt, and the V^T tile of kt (the half is part of the V^T XOR).
+    auto kunit = [&](int kt, int half) __attribute__((always_inline)) {
+        return (uint32_t)(buf_of(kt) - smem) + A0 + (uint32_t)(half * 32 * T::KROW);
     };
-    // Keys >= nk of the last tile get -inf scores.
-    auto mask = [&](f32x16 (&s)[2], int kt) __attribute__((always_inline)) {
+    auto vtile = [&](int kt) __attribute__((always_inline)) { return (uint32_t)(buf_of(kt) - smem) + B0; };
+    auto kread = [&](uint32_t kb, int j) __attribute__((always_inline)) { return lds_read16(kb ^ (uint32_t)(32 * j)); };
+    // V^T operand read r = g * DT + c of the unit (half) of a tile
+    auto vread = [&](uint32_t vb, int half, int r) __attribute__((always_inline)) {
+        const int g = r / DT, c = r % DT;
+        return lds_read16((vb ^ (uint32_t)(64 * half + 32 * g)) + c * 32 * T::VROW);
+    };
+    // Keys >= nk of unit (kt, half) get -inf scores.
+    auto mask = [&](f32x16 (&s)[QB], int kt, int half) __attribute__((always_inline)) {
         if (ragged && kt + 1 == ntiles_all) {
-            // key (tile-relative) = 32 tt + 8 (i / 4) + 4 hf + i % 4 is masked when >= nk - k0
-            const int lim = (int)(a.nk - (int64_t)kt * BN) - 4 * hf;
+            drain_s(s);  // the products forming these scores may still be in flight
+            const int lim = (int)(a.nk - (int64_t)kt * BN) - 32 * half - 4 * hf;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int b = 0; b < QB; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (32 * tt + 8 * (i >> 2) + (i & 3) >= lim) s[tt][i] = -__builtin_inff();
+                    if (8 * (i >> 2) + (i & 3) >= lim) s[b][i] = -__builtin_inff();
         }
-    };
-    auto tile_max = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
-        float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-        for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-        return fmaxf(mx, half_swap_partner(mx));  // both half-waves hold the same query
-    };
-    // For each 16-key group (tt, g): P = 2^s rounded to bf16 (already in the
-    // B-operand layout of O^T += V^T P^T), l += the sum of those bf16 values,
-    // then the four d-tiles' products with that group. The next group's
-    // exponentials overlap this group's matrix-core work.
-    auto exp_pv = [&](const unsigned char *buf, const f32x16 (&s)[2], const float m) __attribute__((always_inline)) {
-        const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
-        auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
-            return lds_read16((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW);
-        };
-        float ls[2] = {0.f, 0.f};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                bf16x8 pv;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    bf16x2 pp;
-                    pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e] - m);
-                    pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e + 1] - m);
-                    ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
-                    pv[e] = pp.x;
-                    pv[e + 1] = pp.y;
-                }
-#pragma unroll
-                for (int c = 0; c < DT; ++c)
-                    o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(c, tt, g), pv, o[c], 0, 0, 0);
-            }
-        l += ls[0] + ls[1];
     };
 
-    // Hot-loop block, scheduled by hand: the scores of the next tile (QK) and
-    // the softmax + P.V of this tile, in four 16-key groups. Each group first
-    // issues its four V^T operand reads, then runs two k-steps of the next
-    // tile's Q.K^T (K operands read two steps ahead) interleaved with its
-    // exponentials, then its four P.V products. Every operand read is issued
-    // several matrix-core ops before its use, so LDS latency stays hidden;
-    // sched_barrier pins the order. The wave raises its issue priority while
-    // it issues matrix-core ops, so the SIMD's other wave, when it has VALU
-    // work, does not hold them back (the matrix core stays fed).
-    auto qk_exp_pv = [&](const unsigned char *nbuf, f32x16 (&sn)[2], const unsigned char *buf,
-                         const f32x16 (&s)[2]) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t kb0 = (uint32_t)(nbuf - smem) + A0;
-        const uint32_t vb0 = (uint32_t)(buf - smem) + B0;
-        auto kread = [&](int j, int tt) __attribute__((always_inline)) {
-            return lds_read16((kb0 ^ (uint32_t)(32 * j)) + tt * 32 * T::KROW);
-        };
-        auto vread = [&](int c, int tt, int g) __attribute__((always_inline)) {
-            return lds_read16((vb0 ^ (uint32_t)(64 * tt + 32 * g)) + c * 32 * T::VROW);
-        };
-        constexpr int KSTEPS_PER_GROUP = DC / 4;
-        bf16x8 kr[DC][2];
-        kr[0][0] = kread(0, 0);
-        kr[0][1] = kread(0, 1);
-        if (DC > 1) {
-            kr[1][0] = kread(1, 0);
-            kr[1][1] = kread(1, 1);
-        }
-        float ls[2] = {0.f, 0.f};
+    // Plain Q.K^T of one unit for every block (pipeline prologue, second pass).
+    auto qk_unit = [&](uint32_t kb, f32x16 (&s)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-            const int tt = grp >> 1, g = grp & 1;
-            bf16x8 vr[DT];
+        for (int j = 0; j < DC; ++j) {
+            const bf16x8 kr = kread(kb, j);
 #pragma unroll
-            for (int c = 0; c < DT; ++c) vr[c] = vread(c, tt, g);
-            bf16x8 pv;
-#pragma unroll
-            for (int h = 0; h < KSTEPS_PER_GROUP; ++h) {
-                const int j = grp * KSTEPS_PER_GROUP + h;
-                if (j + 2 < DC) {
-                    kr[j + 2][0] = kread(j + 2, 0);
-                    kr[j + 2][1] = kread(j + 2, 1);
+            for (int b = 0; b < QB; ++b) {
+                if (b < QA) {
+                    if (j) mfma_qk<ROTK>(s[b], kr, qreg[b][j]);
+                    else mfma_qk0<ROTK>(s[b], kr, qreg[b][j]);
+                } else {
+                    if (j) mfma_qk_v<ROTK>(s[b], kr, qreg[b][j]);
+                    else mfma_qk0_v<ROTK>(s[b], kr, qreg[b][j]);
                 }
-                __builtin_amdgcn_s_setprio(1);
-                sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][0], qreg[j], j ? sn[0] : zero16, 0, 0, 0);
-                sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[j][1], qreg[j], j ? sn[1] : zero16, 0, 0, 0);
-                __builtin_amdgcn_s_setprio(0);
-                // this k-step's share of the group's exponentials
-                constexpr int E = 8 / KSTEPS_PER_GROUP;
+            }
+        }
+        drain_s(s);
+    };
+    // Plain exponentials of one unit with anchor m[b]: P (bf16, B-operand layout
+    // of O^T += V^T P^T) and row sums.
+    auto exp_unit = [&](f32x16 (&s)[QB], bf16x8 (&p)[QB][2], const float (&m)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int e = h * E; e < (h + 1) * E; e += 2) {
-                    bf16x2 pp;
-                    pp.x = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e]);
-                    pp.y = (bf16)__builtin_amdgcn_exp2f(s[tt][8 * g + e + 1]);
-                    ls[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[g], false);
-                    pv[e] = pp.x;
-                    pv[e + 1] = pp.y;
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float x = __builtin_amdgcn_exp2f(s[b][i] - m[b]);
+                l[b] += x;
+                p[b][i >> 3][i & 7] = (bf16)x;
+            }
+    };
+
+    // Order of the matrix-core ops of one pipeline stage: NPV P.V products of
+    // unit i (index m: V^T read r = m / QB, block b = m % QB) and NQK Q.K^T
+    // products of unit i+2 (index m: k-step j = m / QB, block b = m % QB). The
+    // first LEAD slots are P.V products (their operands were read ahead by the
+    // previous stage), then the two kinds alternate until one runs out. Operands
+    // are read LK k-steps / LV V^T reads ahead of their first use; a read serves
+    // all QB blocks.
+    constexpr int NPV = QB * NVR;
+    constexpr int NQK = QB * DC;
+    constexpr int LEAD = 4;
+    constexpr int LK = 3;
+    constexpr int LV = 3;
+    constexpr int EOFF = 2;  // first exponential two slots into the stage
+
+    auto stage = [&](auto QK_, auto EX_, auto KPRE_, auto NXK_, auto NXV_, uint32_t kb, uint32_t nkb, uint32_t vb,
+                     int vhalf, uint32_t nvb, int nvhalf, f32x16 (&sw)[QB], f32x16 (&sr)[QB],
+                     const bf16x8 (&pv)[QB][2], bf16x8 (&pw)[QB][2], bf16x8 (&kpre)[LK], bf16x8 (&vpre)[LV])
+        __attribute__((always_inline)) {
+        constexpr bool QK = decltype(QK_)::value;
+        constexpr bool EX = decltype(EX_)::value;
+        constexpr bool KPRE = decltype(KPRE_)::value;
+        constexpr bool NXK = decltype(NXK_)::value;
+        constexpr bool NXV = decltype(NXV_)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 vr[NVR + LV];
+        bf16x8 kr[DC + LK];
+#pragma unroll
+        for (int r = 0; r < LV; ++r) vr[r] = vpre[r];
+        if constexpr (QK) {
+#pragma unroll
+            for (int j = 0; j < LK; ++j) kr[j] = KPRE ? kpre[j] : kread(kb, j);
+        }
+        int qk_m = 0, pv_m = 0;
+        constexpr int NS = (QK ? NQK : 0) + NPV;
+        constexpr int NV = QB * 16;
+        constexpr int PER = NV / NS > 1 ? NV / NS : 1;  // exponentials per slot
+        float ls[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) ls[b] = 0.f;
+        auto exp_v = [&](int v) __attribute__((always_inline)) {
+            sr[v >> 4][v & 15] = __builtin_amdgcn_exp2f(sr[v >> 4][v & 15]);
+        };
+        auto sum_pack_v = [&](int v) __attribute__((always_inline)) {
+            const int b = v >> 4, i = v & 15;
+            ls[b] += sr[b][i];
+            asm volatile("" :: "v"(ls[b]));
+            if (i & 1) {
+                bf16x2 pp;
+                pp.x = (bf16)sr[b][i - 1];
+                pp.y = (bf16)sr[b][i];
+                uint32_t u = __builtin_bit_cast(uint32_t, pp);
+                asm volatile("" : "+v"(u));
+                pw[b][i >> 3][(i & 7) - 1] = __builtin_bit_cast(bf16x2, u).x;
+                pw[b][i >> 3][i & 7] = __builtin_bit_cast(bf16x2, u).y;
+            }
+        };
+#pragma unroll
+        for (int slot = 0; slot < NS; ++slot) {
+            bool is_pv;
+            if (!QK) is_pv = true;
+            else if (slot < LEAD) is_pv = true;
+            else if (pv_m >= NPV) is_pv = false;
+            else if (qk_m >= NQK) is_pv = true;
+            else is_pv = ((slot - LEAD) & 1) != 0;
+            // matrix-core op first, then this slot's operand reads, then its VALU work
+            if (is_pv) {
+                const int r = pv_m / QB, b = pv_m % QB;
+                mfma_pv<ROTK>(o[b][r % DT], vr[r], pv[b][r / DT]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (b == 0) {
+                    if (r + LV < NVR) vr[r + LV] = vread(vb, vhalf, r + LV);
+                    else if (NXV) vpre[r + LV - NVR] = vread(nvb, nvhalf, r + LV - NVR);
+                }
+                ++pv_m;
+            } else {
+                const int j = qk_m / QB, b = qk_m % QB;
+                if (b < QA) {
+                    if (j == 0) mfma_qk0<ROTK>(sw[b], kr[0], qreg[b][0]);
+                    else mfma_qk<ROTK>(sw[b], kr[j], qreg[b][j]);
+                } else {
+                    if (j == 0) mfma_qk0_v<ROTK>(sw[b], kr[0], qreg[b][0]);
+                    else mfma_qk_v<ROTK>(sw[b], kr[j], qreg[b][j]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                if (b == 0) {
+                    if (j + LK < DC) kr[j + LK] = kread(kb, j + LK);
+                    else if (NXK) kpre[j + LK - DC] = kread(nkb, j + LK - DC);
+                }
+                ++qk_m;
             }
-            __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (EX) {
+                const int es = slot - EOFF;
+                if (es >= 0)
 #pragma unroll
-            for (int c = 0; c < DT; ++c) o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c], pv, o[c], 0, 0, 0);
-            __builtin_amdgcn_s_setprio(0);
+                    for (int q = 0; q < PER; ++q)
+                        if (es * PER + q < NV) exp_v(es * PER + q);
+                const int as = slot - EOFF - 2;
+                if (as >= 0)
+#pragma unroll
+                    for (int q = 0; q < PER; ++q)
+                        if (as * PER + q < NV) sum_pack_v(as * PER + q);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        l += ls[0] + ls[1];
+        if constexpr (EX) {
+            // exponentials, sums and packs left after the last slot
+#pragma unroll
+            for (int v = (NS - EOFF) * PER; v < NV; ++v) exp_v(v);
+#pragma unroll
+            for (int v = (NS - EOFF - 2) * PER; v < NV; ++v) sum_pack_v(v);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) l[b] += ls[b];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) asm volatile("" :: "v"(l[b]), "v"(pw[b][0]), "v"(pw[b][1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Output of this lane's half of row q_row: O^T column l32, d-rows
-    // 32 c + 8 g + 4 hf .. +3 of each 32-row d tile.
-    auto store = [&](float lsum, float m) __attribute__((always_inline)) {
+    auto store = [&](int b, float lsum, float m) __attribute__((always_inline)) {
+        const int64_t q_row = row0 + 32 * b;
         const float inv = 1.0f / lsum;
-        if (a.partial || a.tail_units) {  // split-KV: normalised partial output and natural log-sum-exp
+        if (a.partial || a.tail_units) {
             const int64_t prow = a.tail_units ? ((int64_t)tail_unit * 2 + split) * BM + (q_row - (int64_t)qt * BM)
                                               : ((int64_t)split * a.nq + q_row) * a.heads + head;
             float *pp = (a.tail_units ? a.tail_part : a.partial) + prow * D;
@@ -482,10 +549,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     f32x4 r;
-                    r.x = o[c][4 * g + 0] * inv;
-                    r.y = o[c][4 * g + 1] * inv;
-                    r.z = o[c][4 * g + 2] * inv;
-                    r.w = o[c][4 * g + 3] * inv;
+                    r.x = o[b][c][4 * g + 0] * inv;
+                    r.y = o[b][c][4 * g + 1] * inv;
+                    r.z = o[b][c][4 * g + 2] * inv;
+                    r.w = o[b][c][4 * g + 3] * inv;
                     *reinterpret_cast<f32x4 *>(pp + 32 * c + 8 * g + 4 * hf) = r;
                 }
             if (hf == 0) (a.tail_units ? a.tail_lse : a.lse)[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
@@ -498,148 +565,183 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int g = 0; g < 4; ++g) {
                 const int d0 = 32 * c + 8 * g + 4 * hf;
                 f32x4 r;
-                r.x = o[c][4 * g + 0] * inv;
-                r.y = o[c][4 * g + 1] * inv;
-                r.z = o[c][4 * g + 2] * inv;
-                r.w = o[c][4 * g + 3] * inv;
+                r.x = o[b][c][4 * g + 0] * inv;
+                r.y = o[b][c][4 * g + 1] * inv;
+                r.z = o[b][c][4 * g + 2] * inv;
+                r.w = o[b][c][4 * g + 3] * inv;
                 if (OUT_F32) {
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + obase + d0) = r;
                 } else {
-                    bf16x4 b;
-                    b.x = (bf16)r.x;
-                    b.y = (bf16)r.y;
-                    b.z = (bf16)r.z;
-                    b.w = (bf16)r.w;
-                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.out) + obase + d0) = b;
+                    bf16x4 bb;
+                    bb.x = (bf16)r.x;
+                    bb.y = (bf16)r.y;
+                    bb.z = (bf16)r.z;
+                    bb.w = (bf16)r.w;
+                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(a.out) + obase + d0) = bb;
                 }
             }
     };
 
-    // ---- main pass: running max held at 0 ----------------------------------
-    // Softmax is invariant to the max it subtracts; holding it at 0 is exact
-    // as long as nothing over- or underflows: P = 2^s stays a normal float for
-    // s in (-126, 128), and the row's result is then the same as with any other
-    // anchor up to rounding. That is checked once per row at the end (row sum
-    // within [2^-100, 2^100], O finite); a row that fails is recomputed by the
-    // second pass below with an explicit running max. While the softmax of tile
-    // kt runs on the VALU, the matrix cores already form the scores of tile
-    // kt+1.
+    // ---- main pass: running max held at 0, a three-stage unit pipeline ----
     issue(t_begin);
     issue(t_begin + 1);
     end_tile();
-    // Two score sets alternate roles (unrolled by two), so no copy of the
-    // next tile's scores is needed between tiles.
-    f32x16 s[2], sb[2];
     if constexpr (ROTK) rotate_k(t_begin);
-    // A wave whose 32 query rows all lie past nq (the last query tile of a
-    // short call) computes nothing; it still issues its share of every tile
-    // load and meets every barrier, in the same order as the other waves.
-    const bool wave_has_rows = (int64_t)qt * BM + wu * 32 < a.nq;
+    const bool wave_has_rows = (int64_t)qt * BM + wu * (QB * 32) < a.nq;
     if (wave_has_rows) {
-        qk(buf_of(t_begin), s, zero16);
+        // S of units 0 and 1 (tile t_begin), P of unit 0.
+        f32x16 sA[QB], sB[QB];
+        bf16x8 pA[QB][2], pB[QB][2];
+        bf16x8 kpre[LK], vpre[LV];
+        qk_unit(kunit(t_begin, 0), sA);
+        qk_unit(kunit(t_begin, 1), sB);
+        mask(sA, t_begin, 0);
+        float zero_m[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) zero_m[b] = 0.f;
+        exp_unit(sA, pA, zero_m);
+        valu_to_mfma(pA);
+#pragma unroll
+        for (int r = 0; r < LV; ++r) vpre[r] = vread(vtile(t_begin), 0, r);
+        // Stage i = 2 kt' + h: P.V of unit i (tile kt, half h), Q.K^T of unit
+        // i + 2 (tile kt + 1, half h), exponentials of unit i + 1. S of unit u
+        // lives in sA when u is even, sB when odd; P likewise in pA / pB.
         int kt = t_begin;
-        for (; kt + 1 < ntiles; kt += 2) {
+        for (; kt + 1 < ntiles; ++kt) {
             if constexpr (ROTK) rotate_k(kt + 1);
-            issue(kt + 2);
-            mask(s, kt);
-            qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
-            end_tile();
-            if constexpr (ROTK) rotate_k(kt + 2);
-            issue(kt + 3);
-            mask(sb, kt + 1);
-            qk_exp_pv(buf_of(kt + 2), s, buf_of(kt + 1), sb);
+            issue(kt + NSTAGE - 1);
+            mask(sB, kt, 1);
+            stage(bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), bconst<true>(), kunit(kt + 1, 0),
+                  kunit(kt + 1, 1), vtile(kt), 0, vtile(kt), 1, sA, sB, pA, pB, kpre, vpre);
+            mask(sA, kt + 1, 0);
+            stage(bconst<true>(), bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), kunit(kt + 1, 1),
+                  0u, vtile(kt), 1, vtile(kt + 1), 0, sB, sA, pB, pA, kpre, vpre);
             end_tile();
         }
-        if (kt < ntiles) {
-            // Last (odd) tile: the next-tile scores read a resident buffer and
-            // are discarded.
-            if constexpr (ROTK) rotate_k(kt + 1);
-            issue(kt + 2);
-            mask(s, kt);
-            qk_exp_pv(buf_of(kt + 1), sb, buf_of(kt), s);
-            end_tile();
-        }
+        // last tile: P.V of its two units, exponentials of its second unit
+        if constexpr (ROTK) rotate_k(kt + 1);
+        issue(kt + NSTAGE - 1);
+        mask(sB, kt, 1);
+        stage(bconst<false>(), bconst<true>(), bconst<false>(), bconst<false>(), bconst<true>(), 0u, 0u, vtile(kt), 0,
+              vtile(kt), 1, sA, sB, pA, pB, kpre, vpre);
+        stage(bconst<false>(), bconst<false>(), bconst<false>(), bconst<false>(), bconst<false>(), 0u, 0u, vtile(kt),
+              1, 0u, 0, sB, sA, pB, pA, kpre, vpre);
+        // Before the join below, where the compiler may move the accumulators
+        // between registers: no copy may read a product still in flight.
+        drain_o(o);
+        end_tile();
     } else {
+        // A wave whose query rows all lie past nq (in the last query tile)
+        // computes nothing, but issues its share of every tile load and meets
+        // every barrier in the same order as its workgroup.
         for (int kt = t_begin; kt < ntiles; ++kt) {
             if constexpr (ROTK) rotate_k(kt + 1);
-            issue(kt + 2);
+            issue(kt + NSTAGE - 1);
             end_tile();
         }
     }
 
     // ---- per-row check and store ----------------------------------------------
-    float lt = l + half_swap_partner(l);
-    float osum = 0.f;  // any inf or NaN in O propagates into the sum
+    drain_o(o);
+    bool ok[QB], row[QB];
+    float lt[QB];
 #pragma unroll
-    for (int c = 0; c < DT; ++c)
+    for (int b = 0; b < QB; ++b) {
+        lt[b] = l[b] + half_swap_partner(l[b]);
+        float osum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) osum += o[c][i];
-    osum += half_swap_partner(osum);
-    const bool row = q_row < a.nq;
-    const bool ok = lt >= 0x1p-100f && lt <= 0x1p+100f && __builtin_isfinite(osum);
-    if (row && ok) store(lt, 0.0f);
+        for (int c = 0; c < DT; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) osum += o[b][c][i];
+        osum += half_swap_partner(osum);
+        row[b] = row0 + 32 * b < a.nq;
+        ok[b] = lt[b] >= 0x1p-100f && lt[b] <= 0x1p+100f && __builtin_isfinite(osum);
+        if (row[b] && ok[b]) store(b, lt[b], 0.0f);
+    }
 
     // ---- second pass (rare): explicit running max ---------------------------
-    // Taken by the whole workgroup when any of its rows failed the check;
-    // every wave streams the tiles again (one barrier per tile, as in the main
-    // pass), and only failed rows are stored, so a row's output never depends
-    // on its neighbours. Scores are formed as in the main pass and m is
-    // subtracted in the exponent; m is raised when a tile's max exceeds it by
-    // more than 2^8, and O and l are rescaled on every tile (by exactly 1 when
-    // m does not move).
-    // Workgroup vote through LDS: one flag per wave in the buffer of tile
-    // t_begin + 2, which the second pass's first two tile loads (tiles t_begin
-    // and t_begin + 1) do not touch; every wave reads the flags before the
-    // barrier that follows those loads, and only after it is that buffer
-    // loaded again.
-    unsigned *flags = reinterpret_cast<unsigned *>(buf_of(t_begin + 2));
-    const unsigned wave_fail = __any(row && !ok) ? 1u : 0u;  // vote of the whole wave, outside the lane-0 branch
+    unsigned *flags = reinterpret_cast<unsigned *>(buf_of(t_begin + NSTAGE - 1));
+    bool any_row_fails = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) any_row_fails |= row[b] && !ok[b];
+    const unsigned wave_fail = __any(any_row_fails) ? 1u : 0u;
     if (lane == 0) flags[w] = wave_fail;
     __syncthreads();
     unsigned any_fail = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) any_fail |= flags[i];
     if (any_fail) {
+        // Sweep 1: the exact row max (log2 units) over every key.
+        float m[QB];
 #pragma unroll
-        for (int c = 0; c < DT; ++c) o[c] = f32x16{};
-        l = 0.f;
-        float m = 0.f;
+        for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
         issue(t_begin);
         issue(t_begin + 1);
         end_tile();
         for (int kt = t_begin; kt < ntiles; ++kt) {
             if constexpr (ROTK) rotate_k(kt);
-            issue(kt + 2);
-            qk(buf_of(kt), s, zero16);
-            mask(s, kt);
-            const float mx = tile_max(s);  // absolute tile max (log2 units)
-            float mnew;
-            if (kt == t_begin)  // nothing accumulated yet: adopt the first tile's max if out of band
-                mnew = (mx > kLazyRescale || mx < -kLazyRescale) ? mx : 0.0f;
-            else
-                mnew = (mx - m > kLazyRescale) ? mx : m;
-            const float alpha = kt == t_begin ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
-            l *= alpha;
+            issue(kt + NSTAGE - 1);
 #pragma unroll
-            for (int c = 0; c < DT; ++c) o[c] *= alpha;
-            m = mnew;
-            exp_pv(buf_of(kt), s, m);
+            for (int h = 0; h < 2; ++h) {
+                f32x16 s[QB];
+                qk_unit(kunit(kt, h), s);
+                mask(s, kt, h);
+#pragma unroll
+                for (int b = 0; b < QB; ++b) {
+                    float mx = s[b][0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+                    m[b] = fmaxf(m[b], fmaxf(mx, half_swap_partner(mx)));
+                }
+            }
             end_tile();
         }
-        lt = l + half_swap_partner(l);
-        if (row && !ok) store(lt, m);
+        // Sweep 2: P = 2^(s - m), row sums and P.V with that fixed anchor.
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+#pragma unroll
+            for (int c = 0; c < DT; ++c) o[b][c] = f32x16{};
+            l[b] = 0.f;
+        }
+        issue(t_begin);
+        issue(t_begin + 1);
+        end_tile();
+        for (int kt = t_begin; kt < ntiles; ++kt) {
+            if constexpr (ROTK) rotate_k(kt);
+            issue(kt + NSTAGE - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x16 s[QB];
+                bf16x8 p[QB][2];
+                qk_unit(kunit(kt, h), s);
+                mask(s, kt, h);
+                exp_unit(s, p, m);
+                valu_to_mfma(p);
+                const uint32_t vb = vtile(kt);
+#pragma unroll
+                for (int r = 0; r < NVR; ++r) {
+                    const bf16x8 vr = vread(vb, h, r);
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) mfma_pv<ROTK>(o[b][r % DT], vr, p[b][r / DT]);
+                }
+            }
+            drain_o(o);  // inside the loop: its exit may move the accumulators between registers
+            end_tile();
+        }
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            lt[b] = l[b] + half_swap_partner(l[b]);
+            if (row[b] && !ok[b]) store(b, lt[b], m[b]);
+        }
     }
 }
 
-constexpr int kNW = 8;  // waves per workgroup (two per SIMD), 32 queries each
-
 template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
-    constexpr int BM = kNW * 32;
-    const int64_t n_qt = (a.nq + BM - 1) / BM;
+    const int64_t n_qt = (a.nq + kBM - 1) / kBM;
     const int64_t nwg = a.tail_units ? 2 * (int64_t)a.tail_units
                                      : a.grid_units ? (int64_t)a.grid_units : n_qt * a.heads * a.n_splits;
-    auto kern = a.k_table ? fwd_bf16_kernel<D, kNW, OUT_F32, true> : fwd_bf16_kernel<D, kNW, OUT_F32, false>;
+    auto kern = a.k_table ? fwd_bf16_kernel<D, OUT_F32, true> : fwd_bf16_kernel<D, OUT_F32, false>;
     constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,
     // idempotent, no stream work).
@@ -652,7 +754,7 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-int fwd_bf16_rows_per_workgroup() { return kNW * 32; }
+int fwd_bf16_rows_per_workgroup() { return kBM; }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t stream) {
     if (a.nq == 0) return hipSuccess;

@@ -209,6 +209,12 @@ class TierStreamAttention:
         raw keys / values, ``[chunk_rows][heads][head_dim]`` device tensors
         the stream keeps (by reference) while the chunk is in the context.
         Rewrites the dynamic region and runs the forward; returns the output."""
+        self.age(k, v, stream)
+        return self.forward(q, stream)
+
+    def age(self, k, v, stream=None):
+        """Enter the next chunk's keys and values: every history tier moves
+        one step older and the dynamic region is packed again in place."""
         st = self.st
         self.history.append((k, v))
         self.chunk += 1
@@ -223,9 +229,12 @@ class TierStreamAttention:
         row += k.shape[0]
         self.ctx.rows = row
         B.sa_pack_context(self.ctx, segs, stream=stream)
+
+    def forward(self, q, stream=None):
+        """Attention of the current chunk's queries over the packed context."""
         ws = B.sa_forward_workspace_bytes(self.ctx, q.shape[0])
         if ws and (self.workspace is None or self.workspace.numel() < ws):
             self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
-        B.sa_forward_ws(self.ctx, q, self.q_table, st.scale, out=self.out, stream=stream,
+        B.sa_forward_ws(self.ctx, q, self.q_table, self.st.scale, out=self.out, stream=stream,
                         workspace=self.workspace if ws else None)
         return self.out

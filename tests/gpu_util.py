@@ -38,9 +38,10 @@ def assert_parity(got, ref, dtype, what=""):
 
 
 def sample_rows(nq, extra=48, seed=0):
-    """Rows that cross 32/64/256-row tile edges, the ragged tail, plus random ones."""
+    """Rows that cross the 32-row query blocks, 64-row key tiles, 96-row wave
+    and 384-row workgroup edges, the ragged tail, plus random ones."""
     edges = []
-    for b in (32, 64, 256):
+    for b in (32, 64, 96, 384):
         for k in range(1, nq // b + 1):
             for r in (k * b - 1, k * b):
                 if 0 <= r < nq:
@@ -82,3 +83,16 @@ def oracle(ca, rows=None):
     w = ca.w
     return attn64.chunk_attention(q, q_pos, attention_segments(segs), w.axis_dims, w.theta, w.scale, rows=rows,
                                   q_norm=qn, k_norm=kn)
+
+
+def rows_per_workgroup():
+    """Query rows per (head, query tile) unit of the bf16 forward, read off the
+    workspace the library asks for: n_cu + 1 heads of one query row make a
+    second round holding a single unit, whose two key halves take
+    2 * rows * (head_dim + 1) * 4 bytes."""
+    import torch
+    from streaming_video_diffusion_amd import binding as B
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx = B.PackedContext(n_cu + 1, 128, torch.bfloat16, 128, device="cuda")
+    ctx.rows = 128
+    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * 129 * 4)

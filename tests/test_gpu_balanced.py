@@ -9,19 +9,16 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_parity, note, oracle, run, sample_rows
+from gpu_util import assert_parity, note, oracle, rows_per_workgroup, run, sample_rows
 from streaming_video_diffusion_amd import binding as B
 from streaming_video_diffusion_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-BM = 256  # query rows per (head, query tile) unit of the bf16 forward
-
-
 def plan(nq, heads):
     """(units in the tail, first tail unit) as the library plans them on this GPU."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    units = math.ceil(nq / BM) * heads
+    units = math.ceil(nq / rows_per_workgroup()) * heads
     rounds = math.ceil(units / n_cu)
     r = units - (rounds - 1) * n_cu
     if rounds < 2 or 2 * r > n_cu:
@@ -31,6 +28,7 @@ def plan(nq, heads):
 
 def tail_mask(nq, heads, first_unit):
     """[nq][heads] True where the (row, head) belongs to a tail unit."""
+    BM = rows_per_workgroup()
     n_qt = math.ceil(nq / BM)
     m = np.zeros((nq, heads), dtype=bool)
     for u in range(first_unit, n_qt * heads):
@@ -42,7 +40,7 @@ def tail_mask(nq, heads, first_unit):
 def balanced_case():
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     heads = n_cu // 8            # 9 query tiles x n_cu/8 heads = n_cu + n_cu/8 units: a tail of n_cu/8
-    return I.custom("balanced", 600, "bf16", heads, 128, [150, 130], 9 * BM - 100, prompt_rows=20)
+    return I.custom("balanced", 600, "bf16", heads, 128, [150, 130], 9 * rows_per_workgroup() - 100, prompt_rows=20)
 
 
 def test_workspace_bytes_follow_the_rounds():
@@ -50,7 +48,7 @@ def test_workspace_bytes_follow_the_rounds():
         ctx = B.PackedContext(w.heads, w.head_dim, torch.bfloat16, w.nk)
         ctx.rows = w.nk
         r, _ = plan(w.nq, w.heads)
-        assert B.sa_forward_workspace_bytes(ctx, w.nq) == 2 * r * BM * (w.head_dim + 1) * 4, w.name
+        assert B.sa_forward_workspace_bytes(ctx, w.nq) == 2 * r * rows_per_workgroup() * (w.head_dim + 1) * 4, w.name
 
 
 @pytest.mark.parametrize("out_dtype", [None, torch.float32], ids=["out_bf16", "out_f32"])

@@ -1,6 +1,6 @@
 """Seeded random shapes against the fp64 oracle: heads, head dim, dtype,
 segment sizes (empty, single rows, tile edges), prompt rows, query counts
-around the 32/64/256-row tile edges, QK-norm and output dtype drawn per case;
+around the 32/64/96/384-row block, tile, wave and workgroup edges, QK-norm and output dtype drawn per case;
 each case through the chunk sequence and through split-KV plus the merge."""
 
 import numpy as np
@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 16
 ROWS = [0, 1, 17, 63, 64, 65, 100, 129, 200, 333]
-NQ = [1, 31, 32, 63, 65, 255, 256, 257, 300]
+NQ = [1, 31, 32, 63, 65, 95, 97, 255, 257, 383, 385, 400]
 
 
 def draw(i):
