@@ -43,24 +43,25 @@ TRAFFIC = {
 
 
 def bf16_rows_per_workgroup():
-    """Query rows per workgroup of the bf16 forward, read off the workspace
-    the library asks for: n_cu + 1 heads of one query row leave one unit in a
-    second round, whose two key halves take 2 * rows * (d + 1) * 4 bytes."""
+    """Query rows per (head, query tile) unit of the bf16 forward, read off the
+    workspace the library asks for: n_cu / 2 heads of one query row over 16 key
+    tiles make one part-empty round of n_cu / 2 units, which the stream-K tail
+    spreads over every CU, with 2 * n_cu slots of rows * (head_dim + 1) floats."""
     import torch
     from streaming_video_diffusion_amd import binding as B
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    ctx = B.PackedContext(n_cu + 1, 128, torch.bfloat16, 128, device="cuda")
-    ctx.rows = 128
-    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * 129 * 4)
+    ctx = B.PackedContext(n_cu // 2, 128, torch.bfloat16, 1024, device="cuda")
+    ctx.rows = 1024
+    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * n_cu * 129 * 4)
 
 
 def fwd_kernel_name(ca):
     bm = bf16_rows_per_workgroup()
     units = -(-ca.w.nq // bm) * ca.w.heads
     if ca.workspace is not None:
-        return (f"fwd_bf16_kernel<128, false, false> ({units} units of {bm} queries, the last round's as key "
-                f"halves) + tail_combine_kernel<128, false>")
-    return f"fwd_bf16_kernel<128, false, false> ({units} workgroups of {bm} queries)"
+        return (f"fwd_bf16_kernel<128, false, false, *> ({units} units of {bm} queries, the last round's spread "
+                f"over every CU) + tail_combine_kernel<128, false>")
+    return f"fwd_bf16_kernel<128, false, false, false> ({units} workgroups of {bm} queries)"
 
 
 def parse():

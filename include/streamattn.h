@@ -62,9 +62,9 @@ extern "C" {
 /* Largest spatial pooling factor of a segment (sa_segment.pool). */
 #define SA_MAX_POOL 8
 /* Bytes of device scratch sa_forward_noalloc holds on each device it runs on
- * (64 MiB: the balanced last round needs at most 50.7 MB at head_dim 128 on
- * 256 compute units). */
-#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ * (128 MiB: the stream-K tail needs at most 101.4 MB at head_dim 128 on 256
+ * compute units). */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef int32_t sa_status;
 #define SA_OK 0
@@ -288,7 +288,7 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
 
 /*
  * sa_forward_ws -- sa_forward with a caller workspace that lets the bf16
- * forward balance its last round of workgroups.
+ * forward fill the chip in its last round of workgroups.
  *
  * The operation is sa_forward's (same passages); the workspace only changes
  * how the work is spread over the chip, in the spirit of the pages' attention
@@ -297,11 +297,14 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
  *
  * The bf16 forward runs one workgroup per (head, 384-query tile) unit and one
  * workgroup per compute unit at a time, so W units take ceil(W / n_cu)
- * rounds. When the last round would be at most half full (e.g. 1040 units on
- * 256 CUs: 4.06 rounds run as 5), its r units are computed first as 2r key halves
- * (half a round) into the workspace, the other W - r units as usual, and the
- * halves merged by their log-sum-exps (the identity sa_forward_split rests
- * on): the same result as sa_forward up to rounding, in fewer rounds.
+ * rounds, the last holding r units. When that round would leave at least a
+ * quarter of the CUs idle (e.g. one GPU's 5-head share of the 1344x768 chunk:
+ * 160 units on 256 CUs), its r units are spread over all n_cu CUs instead
+ * (stream-K): their key tiles form one range that is cut into n_cu equal
+ * contiguous pieces; a unit that a cut splits is computed piecewise into the
+ * workspace and the pieces merged by their log-sum-exps (the identity
+ * sa_forward_split rests on), the other units run as usual. Same result as
+ * sa_forward up to rounding, in fewer rounds.
  * workspace: device, 16-byte aligned, at least sa_forward_workspace_bytes()
  *            bytes for this context and nq on the current device; NULL (or a
  *            forward that gains nothing) runs exactly sa_forward. Calls that
@@ -318,8 +321,8 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
  * sa_forward_noalloc -- sa_forward_ws for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc. It computes exactly what sa_forward_ws computes with a
- * large enough workspace (same kernels, same launches), but the balanced last
- * round's scratch is a device array the library holds, SA_NOALLOC_SCRATCH_BYTES
+ * large enough workspace (same kernels, same launches), but the stream-K
+ * tail's scratch is a device array the library holds, SA_NOALLOC_SCRATCH_BYTES
  * on every device it runs on, from that device's first call until the process
  * ends. The call itself allocates nothing; the caller passes inputs and
  * output as for sa_forward.
@@ -341,8 +344,8 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
  * sa_forward_workspace_bytes -- (see sa_forward_ws for the passages it
  * serves) bytes of workspace sa_forward_ws uses for this
  * context and nq on the current device (0 when it would run as sa_forward):
- * 2 r * 384 * (head_dim + 1) * 4 for the r balanced units, at most
- * n_cu * 384 * (head_dim + 1) * 4 (50.7 MB at head_dim 128 on 256 CUs).
+ * 2 * n_cu * 384 * (head_dim + 1) * 4 when the stream-K tail is used (101.4 MB
+ * at head_dim 128 on 256 CUs).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, and the context checks of sa_forward.
  */
 sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes);

@@ -21,7 +21,7 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_ROW_ALIGN = 64
 SA_MAX_SEGMENTS = 16
-SA_NOALLOC_SCRATCH_BYTES = 64 << 20  # device scratch sa_forward_noalloc holds per device
+SA_NOALLOC_SCRATCH_BYTES = 128 << 20  # device scratch sa_forward_noalloc holds per device
 SA_MAX_SPLITS = 256
 
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}

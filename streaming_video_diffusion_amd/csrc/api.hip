@@ -12,8 +12,8 @@
 
 #include "sa_internal.h"
 
-// Scratch of sa_forward_noalloc: the balanced last round's float32 partial
-// outputs and log-sum-exps. Each device the library runs on holds its own copy
+// Scratch of sa_forward_noalloc: the stream-K tail's float32 partial outputs
+// and log-sum-exps. Each device the library runs on holds its own copy
 // until the process ends. In host code this name is only a stand-in: kernels
 // and copies take the device address hipGetSymbolAddress returns for it.
 static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
@@ -331,18 +331,24 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
     return forward_launch(ctx, a, stream);
 }
 
-// Balanced tail of the bf16 forward on the current device: one workgroup per
-// (head, query tile) unit runs per CU at a time, so W units take ceil(W /
-// n_cu) rounds; when the last round is at most half full, its r units are run
-// first as 2r key halves (half a round) and merged, then the other W - r units
-// (whole rounds).
+// Stream-K tail of the bf16 forward on the current device: one workgroup per
+// (head, query tile) unit runs per CU at a time, so W units take
+// ceil(W / n_cu) rounds, the last holding r units. When that round would leave
+// at least a quarter of the CUs idle, its r units are instead spread over all
+// n_cu CUs as equal contiguous ranges of their key tiles (at least 4 tiles per
+// CU), the cut units merged afterwards; the other W - r units run as whole
+// rounds. (With a fuller last round the merge costs about what the idle CUs
+// would: measured level at 216 of 256.)
 struct TailPlan {
     int units = 0;       // r (0: not used)
     int first_unit = 0;  // W - r
+    int wgs = 0;         // workgroups of the tail launch (n_cu)
+    int ntiles = 0;      // key tiles per unit
 };
 static TailPlan tail_plan(const sa_context *ctx, int64_t nq) {
     TailPlan p;
-    if (ctx->dtype != SA_BF16 || nq <= 0) return p;
+    // (The rotate-in-forward build runs every forward as a plain grid.)
+    if (SA_ROTATE_K_IN_FORWARD || ctx->dtype != SA_BF16 || nq <= 0) return p;
     const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
     const int64_t units = (nq + bm - 1) / bm * ctx->heads;
     int dev = 0, n_cu = 0;
@@ -351,13 +357,15 @@ static TailPlan tail_plan(const sa_context *ctx, int64_t nq) {
     const int64_t rounds = (units + n_cu - 1) / n_cu;
     const int64_t r = units - (rounds - 1) * n_cu;
     const int64_t ntiles = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN;
-    if (rounds < 2 || 2 * r > n_cu || ntiles < 2 || units > 0x7fffffff) return p;
+    if (4 * r > 3 * (int64_t)n_cu || r * ntiles < 4 * (int64_t)n_cu || units > 0x7fffffff) return p;
     p.units = (int)r;
     p.first_unit = (int)(units - r);
+    p.wgs = n_cu;
+    p.ntiles = (int)ntiles;
     return p;
 }
-static size_t tail_bytes(int units, int head_dim) {
-    return (size_t)units * 2 * (size_t)sa::fwd_bf16_rows_per_workgroup() * (size_t)(head_dim + 1) * sizeof(float);
+static size_t tail_bytes(const TailPlan &p, int head_dim) {
+    return (size_t)2 * p.wgs * (size_t)sa::fwd_bf16_rows_per_workgroup() * (size_t)(head_dim + 1) * sizeof(float);
 }
 
 sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes) {
@@ -368,29 +376,32 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
     if (st != SA_OK) return st;
     if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
     const TailPlan p = tail_plan(ctx, nq);
-    *bytes = p.units ? tail_bytes(p.units, ctx->head_dim) : 0;
+    *bytes = p.units ? tail_bytes(p, ctx->head_dim) : 0;
     return SA_OK;
 }
 
-// The three launches of a balanced forward (a: validated arguments, p: a plan
-// with units > 0, workspace: device memory of at least tail_bytes(p.units)).
+// The launches of a forward with a stream-K tail (a: validated arguments, p: a
+// plan with units > 0, workspace: device memory of at least tail_bytes(p)).
 static sa_status balanced_launch(const sa_context *ctx, const sa::FwdArgs &a, const TailPlan &p, void *workspace,
                                  hipStream_t stream) {
     const int64_t nq = a.nq;
     const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
     float *part = static_cast<float *>(workspace);
-    float *lse = part + (size_t)p.units * 2 * bm * ctx->head_dim;
-    sa::FwdArgs t = a;  // the tail's key halves first (half a round) ...
+    float *lse = part + (size_t)2 * p.wgs * bm * ctx->head_dim;
+    sa::FwdArgs t = a;  // the tail's ranges of key tiles first (one round) ...
     t.tail_units = p.units;
+    t.tail_wgs = p.wgs;
     t.tail_part = part;
     t.tail_lse = lse;
     hipError_t e = sa::launch_fwd_bf16(t, ctx->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch (tail)");
-    sa::FwdArgs m = a;  // ... then the whole rounds ...
-    m.grid_units = p.first_unit;
-    e = sa::launch_fwd_bf16(m, ctx->head_dim, stream);
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-    sa::TailCombineArgs c{};  // ... and the merge of the halves.
+    if (p.first_unit > 0) {  // ... then the whole rounds ...
+        sa::FwdArgs m = a;
+        m.grid_units = p.first_unit;
+        e = sa::launch_fwd_bf16(m, ctx->head_dim, stream);
+        if (e != hipSuccess) return hip_fail(e, "forward launch");
+    }
+    sa::TailCombineArgs c{};  // ... and the merge of the cut units.
     c.part = part;
     c.lse = lse;
     c.out = a.out;
@@ -402,6 +413,8 @@ static sa_status balanced_launch(const sa_context *ctx, const sa::FwdArgs &a, co
     c.bm = (int)bm;
     c.first_unit = p.first_unit;
     c.units = p.units;
+    c.ntiles = p.ntiles;
+    c.wgs = p.wgs;
     c.out_f32 = a.out_f32;
     e = sa::launch_tail_combine(c, ctx->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "tail merge launch");
@@ -419,7 +432,7 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
     if (st != SA_OK || nq == 0) return st;
     const TailPlan p = tail_plan(ctx, nq);
     if (!p.units || !workspace) return forward_launch(ctx, a, stream);
-    const size_t need = tail_bytes(p.units, ctx->head_dim);
+    const size_t need = tail_bytes(p, ctx->head_dim);
     if (workspace_bytes < need)
         return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -462,7 +475,7 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
     if (st != SA_OK || nq == 0) return st;
     const TailPlan p = tail_plan(ctx, nq);
     if (!p.units) return forward_launch(ctx, a, stream);
-    const size_t need = tail_bytes(p.units, ctx->head_dim);
+    const size_t need = tail_bytes(p, ctx->head_dim);
     if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
         return fail(SA_ERR_CAPACITY, "this forward needs %zu bytes of scratch; sa_forward_noalloc holds %zu",
                     need, (size_t)SA_NOALLOC_SCRATCH_BYTES);

@@ -6,98 +6,123 @@
 // used here to cut the keys of few-query problems into runs processed by
 // separate workgroups. For every (row, head): LSE* = max_s lse_s,
 // w_s = exp(lse_s - LSE*), out = sum_s w_s partial_s / sum_s w_s.
-// One wave per (row, head); each lane owns head_dim / 64 consecutive
-// elements; memory-bound (reads n_splits partial rows, writes one row). The
-// same merge of two key halves finishes a balanced-tail forward.
+// D / 4 lanes per (row, head), 16 bytes each; memory-bound (reads n_splits
+// partial rows, writes one row). The same merge finishes the pieces of the
+// units a stream-K tail cut between workgroups.
 #include "sa_internal.h"
 
 namespace sa {
 
 namespace {
 
-constexpr int kRowsPerBlock = 4;
+constexpr int kThreads = 256;
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store4(void *out, int64_t off, f32x4 v) {
+    if (OUT_F32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + off) = v;
+    } else {
+        bf16x4 b;
+        b.x = (bf16)v.x;
+        b.y = (bf16)v.y;
+        b.z = (bf16)v.z;
+        b.w = (bf16)v.w;
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(out) + off) = b;
+    }
+}
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(CombineArgs a) {
-    constexpr int E = D / 64;  // elements per lane
-    const int64_t rh = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);  // row * heads + head
-    const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+    constexpr int LPR = D / 4;              // lanes per (row, head)
+    constexpr int RPB = kThreads / LPR;     // (row, head) pairs per block
+    const int64_t rh = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;  // row * heads + head
+    const int c = (threadIdx.x % LPR) * 4;
     if (rh >= a.nq * a.heads) return;
     const int64_t row = rh / a.heads;
     const int head = (int)(rh - row * a.heads);
     const int64_t stride = a.nq * a.heads;  // between splits, in (row, head) units
     float mx = -__builtin_inff();
     for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.lse[s * stride + rh]);
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int s = 0; s < a.n_splits; ++s) {
         const float wgt = expf(a.lse[s * stride + rh] - mx);
         wsum += wgt;
-        const float *p = a.partial + (s * stride + rh) * D + lane * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wgt, p[e], acc[e]);
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(a.partial + (s * stride + rh) * D + c);
+        acc.x = __builtin_fmaf(wgt, p.x, acc.x);
+        acc.y = __builtin_fmaf(wgt, p.y, acc.y);
+        acc.z = __builtin_fmaf(wgt, p.z, acc.z);
+        acc.w = __builtin_fmaf(wgt, p.w, acc.w);
     }
     const float inv = 1.0f / wsum;
-    const int64_t obase = row * a.o_rs + (int64_t)head * a.o_hs + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if (OUT_F32)
-            reinterpret_cast<float *>(a.out)[obase + e] = acc[e] * inv;
-        else
-            reinterpret_cast<bf16 *>(a.out)[obase + e] = (bf16)(acc[e] * inv);
-    }
+    const f32x4 r = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    store4<OUT_F32>(a.out, row * a.o_rs + (int64_t)head * a.o_hs + c, r);
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch_t(const CombineArgs &a, hipStream_t stream) {
+    constexpr int RPB = kThreads / (D / 4);
     const int64_t rows = a.nq * a.heads;
-    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL((combine_kernel<D, OUT_F32>), dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0, stream, a);
+    const int64_t blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((combine_kernel<D, OUT_F32>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Merge of a balanced tail: unit u (the (first_unit + u)-th (head, query
-// tile) unit) was computed as two key halves; row r of the unit is query row
-// qt * bm + r of its head. One wave per (unit, row); rows past nq are padding.
+// Merge of the stream-K tail: tail unit ul (the (first_unit + ul)-th (head,
+// query tile) unit) covers tiles [ul T, (ul + 1) T) of the flattened range the
+// tail's G workgroups cut at b_i = floor(i * total / G). The workgroup holding
+// tile x is i(x) = floor(((x + 1) G - 1) / total). A unit inside one
+// workgroup's range was stored whole; a cut unit has one piece per workgroup
+// i0 = i(ul T) .. i1 = i((ul + 1) T - 1) with a non-empty range, in slot 2i
+// when the unit is the first of that range, else 2i + 1. Row r of the unit is
+// query row qt * bm + r of its head; rows past nq are padding.
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void tail_combine_kernel(TailCombineArgs a) {
-    constexpr int E = D / 64;
-    const int64_t ur = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);  // unit * bm + row
-    const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kThreads) void tail_combine_kernel(TailCombineArgs a) {
+    constexpr int LPR = D / 4;
+    constexpr int RPB = kThreads / LPR;
+    const int64_t ur = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;  // unit * bm + row
+    const int c = (threadIdx.x % LPR) * 4;
     if (ur >= (int64_t)a.units * a.bm) return;
-    const int unit = (int)(ur / a.bm);
-    const int r = (int)(ur - (int64_t)unit * a.bm);
-    const int u = a.first_unit + unit;
+    const int ul = (int)(ur / a.bm);
+    const int r = (int)(ur - (int64_t)ul * a.bm);
+    const int u = a.first_unit + ul;
     const int head = u / a.n_qt;
     const int qt = u - head * a.n_qt;
     const int64_t row = (int64_t)qt * a.bm + r;
     if (row >= a.nq) return;
-    const int64_t p0 = ((int64_t)unit * 2) * a.bm + r, p1 = p0 + a.bm;
-    const float l0 = a.lse[p0], l1 = a.lse[p1];
-    const float mx = fmaxf(l0, l1);
-    const float w0 = expf(l0 - mx), w1 = expf(l1 - mx);
-    const float inv = 1.0f / (w0 + w1);
-    const float *x0 = a.part + p0 * D + lane * E;
-    const float *x1 = a.part + p1 * D + lane * E;
-    const int64_t obase = row * a.o_rs + (int64_t)head * a.o_hs + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float v = (w0 * x0[e] + w1 * x1[e]) * inv;
-        if (OUT_F32)
-            reinterpret_cast<float *>(a.out)[obase + e] = v;
-        else
-            reinterpret_cast<bf16 *>(a.out)[obase + e] = (bf16)v;
+    const int64_t T = a.ntiles, G = a.wgs, total = (int64_t)a.units * T;
+    const int64_t x0 = (int64_t)ul * T, x1 = x0 + T - 1;
+    const int i0 = (int)(((x0 + 1) * G - 1) / total), i1 = (int)(((x1 + 1) * G - 1) / total);
+    if (i0 == i1) return;  // stored whole by workgroup i0
+    auto slot_of = [&](int i) { return (i * total / G) / T == ul ? 2 * i : 2 * i + 1; };
+    auto nonempty = [&](int i) { return (int64_t)(i + 1) * total / G > (int64_t)i * total / G; };
+    float mx = -__builtin_inff();
+    for (int i = i0; i <= i1; ++i)
+        if (nonempty(i)) mx = fmaxf(mx, a.lse[(int64_t)slot_of(i) * a.bm + r]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int i = i0; i <= i1; ++i) {
+        if (!nonempty(i)) continue;
+        const int64_t pr = (int64_t)slot_of(i) * a.bm + r;
+        const float wgt = expf(a.lse[pr] - mx);
+        wsum += wgt;
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(a.part + pr * D + c);
+        acc.x = __builtin_fmaf(wgt, p.x, acc.x);
+        acc.y = __builtin_fmaf(wgt, p.y, acc.y);
+        acc.z = __builtin_fmaf(wgt, p.z, acc.z);
+        acc.w = __builtin_fmaf(wgt, p.w, acc.w);
     }
+    const float inv = 1.0f / wsum;
+    const f32x4 res = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    store4<OUT_F32>(a.out, row * a.o_rs + (int64_t)head * a.o_hs + c, res);
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch_tail_t(const TailCombineArgs &a, hipStream_t stream) {
+    constexpr int RPB = kThreads / (D / 4);
     const int64_t rows = (int64_t)a.units * a.bm;
-    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL((tail_combine_kernel<D, OUT_F32>), dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0, stream,
-                       a);
+    const int64_t blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((tail_combine_kernel<D, OUT_F32>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -42,8 +42,9 @@
 //     together on one XCD on the same head, so its K/V tiles hit that XCD's L2;
 //   * the same kernel serves split-KV (each workgroup one run of key tiles,
 //     storing its normalised partial output and natural log-sum-exp) and the
-//     balanced last round (its units as two key halves into a workspace,
-//     merged by tail_combine_kernel).
+//     stream-K tail (the units of a part-empty last round spread over every
+//     CU as equal ranges of key tiles; the units a range boundary cuts are
+//     stored piecewise into a workspace and merged by tail_combine_kernel).
 #include "sa_internal.h"
 
 #include <type_traits>
@@ -198,9 +199,14 @@ __device__ __forceinline__ void valu_to_mfma(bf16x8 (&p)[kQB][2]) {
     asm volatile("s_nop 4" : "+v"(p[0][0]), "+v"(p[0][1]), "+v"(p[1][0]), "+v"(p[1][1]), "+v"(p[2][0]), "+v"(p[2][1]));
 }
 
+// One piece of work: query tile qt of head `head` over key tiles
+// [t_begin, t_end). pslot >= 0: a piece of a unit cut by the stream-K tail,
+// stored as its normalised float32 output and natural log-sum-exp in slot
+// pslot of the tail workspace; with a.partial set, the same for split
+// `split` of a split-KV launch; else the final output is stored.
 template <int D, bool OUT_F32, bool ROTK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const int head, const int split,
+                                          const int t_begin, const int ntiles, const int pslot) {
     constexpr int QB = kQB;           // 32-query blocks per wave
     constexpr int NW = kNW;           // waves, one per SIMD
     constexpr int QA = 2;             // query blocks whose Q lives in AGPRs
@@ -211,27 +217,6 @@ void fwd_bf16_kernel(FwdArgs a) {
     constexpr int NVR = 2 * DT;       // V^T operand reads per 32-key unit
     typedef Tile<D, NW> T;
     extern __shared__ __align__(1024) unsigned char smem[];
-
-    const int nwg = gridDim.x;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const int n_qt = (int)((a.nq + BM - 1) / BM);
-    int qt, head, split, n_splits = a.n_splits, tail_unit = 0;
-    if (a.tail_units) {
-        tail_unit = logical >> 1;
-        split = logical & 1;
-        n_splits = 2;
-        const int u = n_qt * a.heads - a.tail_units + tail_unit;
-        head = u / n_qt;
-        qt = u - head * n_qt;
-    } else {
-        const int hs = logical / n_qt;
-        qt = logical - hs * n_qt;
-        head = hs / a.n_splits;
-        split = hs - head * a.n_splits;
-    }
 
     const int t = threadIdx.x;
     const int w = t >> 6;
@@ -318,8 +303,6 @@ void fwd_bf16_kernel(FwdArgs a) {
         0x00020000);
     const int ntiles_all = (int)((a.nk + BN - 1) / BN);
     const bool ragged = (a.nk % BN) != 0;
-    const int t_begin = split_first_tile(split, n_splits, ntiles_all);
-    const int ntiles = split_first_tile(split + 1, n_splits, ntiles_all);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
     const uint32_t A0 = T::kbase(l32, hf) + lds0;
     const uint32_t B0 = T::vbase(l32, hf) + lds0;
@@ -540,10 +523,10 @@ void fwd_bf16_kernel(FwdArgs a) {
     auto store = [&](int b, float lsum, float m) __attribute__((always_inline)) {
         const int64_t q_row = row0 + 32 * b;
         const float inv = 1.0f / lsum;
-        if (a.partial || a.tail_units) {
-            const int64_t prow = a.tail_units ? ((int64_t)tail_unit * 2 + split) * BM + (q_row - (int64_t)qt * BM)
-                                              : ((int64_t)split * a.nq + q_row) * a.heads + head;
-            float *pp = (a.tail_units ? a.tail_part : a.partial) + prow * D;
+        if (a.partial || pslot >= 0) {
+            const int64_t prow = pslot >= 0 ? (int64_t)pslot * BM + (q_row - (int64_t)qt * BM)
+                                            : ((int64_t)split * a.nq + q_row) * a.heads + head;
+            float *pp = (pslot >= 0 ? a.tail_part : a.partial) + prow * D;
 #pragma unroll
             for (int c = 0; c < DT; ++c)
 #pragma unroll
@@ -555,7 +538,7 @@ void fwd_bf16_kernel(FwdArgs a) {
                     r.w = o[b][c][4 * g + 3] * inv;
                     *reinterpret_cast<f32x4 *>(pp + 32 * c + 8 * g + 4 * hf) = r;
                 }
-            if (hf == 0) (a.tail_units ? a.tail_lse : a.lse)[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
+            if (hf == 0) (pslot >= 0 ? a.tail_lse : a.lse)[prow] = (m + __builtin_log2f(lsum)) * 0.69314718055994531f;
             return;
         }
         const int64_t obase = q_row * a.o_rs + (int64_t)head * a.o_hs;
@@ -583,6 +566,9 @@ void fwd_bf16_kernel(FwdArgs a) {
     };
 
     // ---- main pass: running max held at 0, a three-stage unit pipeline ----
+    // Every wave is done with the LDS of a previous piece (its vote flags)
+    // before the first loads of this one may land there.
+    __syncthreads();
     issue(t_begin);
     issue(t_begin + 1);
     end_tile();
@@ -736,12 +722,71 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
+// Workgroup -> work. The dispatch ids go round-robin over the 8 XCDs; each
+// XCD gets a contiguous range of logical ids, so the workgroups that run
+// together on one XCD share a head's K/V in its L2.
+//   * Plain and split-KV launches: logical id -> (head, split, query tile),
+//     one piece each.
+//   * Stream-K tail (a.tail_units > 0): the last tail_units (head, query
+//     tile) units, each of ntiles key tiles, form one flattened range of
+//     tail_units * ntiles tiles that the nwg workgroups cut into equal
+//     contiguous ranges [b_i, b_i+1), b_i = floor(i * total / nwg). A
+//     workgroup runs the pieces of its range in order: a unit wholly inside
+//     it is stored as the final output; a cut unit's piece goes to slot 2i
+//     (the range's first unit) or 2i + 1 (its last), merged afterwards by
+//     tail_combine_kernel.
+template <int D, bool OUT_F32, bool ROTK, bool TAIL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_kernel(FwdArgs a) {
+    const int nwg = gridDim.x;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int n_qt = (int)((a.nq + kBM - 1) / kBM);
+    const int ntiles_all = (int)((a.nk + BN - 1) / BN);
+    if constexpr (TAIL) {
+        const int64_t total = (int64_t)a.tail_units * ntiles_all;
+        const int64_t b1 = (int64_t)(logical + 1) * total / nwg;
+        int64_t p = (int64_t)logical * total / nwg;
+        const int first = (int)(p / ntiles_all);
+        while (p < b1) {
+            const int ul = (int)(p / ntiles_all);
+            const int t0 = (int)(p - (int64_t)ul * ntiles_all);
+            const int t1 = (int)((int64_t)ntiles_all < t0 + (b1 - p) ? (int64_t)ntiles_all : t0 + (b1 - p));
+            const int u = n_qt * a.heads - a.tail_units + ul;
+            const int head = u / n_qt;
+            const bool whole = t0 == 0 && t1 == ntiles_all;
+            fwd_piece<D, OUT_F32, ROTK>(a, u - head * n_qt, head, 0, t0, t1,
+                                        whole ? -1 : 2 * logical + (ul == first ? 0 : 1));
+            p += t1 - t0;
+        }
+    } else {
+        const int hs = logical / n_qt;
+        const int qt = logical - hs * n_qt;
+        const int head = hs / a.n_splits;
+        const int split = hs - head * a.n_splits;
+        fwd_piece<D, OUT_F32, ROTK>(a, qt, head, split, split_first_tile(split, a.n_splits, ntiles_all),
+                                    split_first_tile(split + 1, a.n_splits, ntiles_all), -1);
+    }
+}
+
 template <int D, bool OUT_F32>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
     const int64_t n_qt = (a.nq + kBM - 1) / kBM;
-    const int64_t nwg = a.tail_units ? 2 * (int64_t)a.tail_units
+    const int64_t nwg = a.tail_units ? (int64_t)a.tail_wgs
                                      : a.grid_units ? (int64_t)a.grid_units : n_qt * a.heads * a.n_splits;
-    auto kern = a.k_table ? fwd_bf16_kernel<D, OUT_F32, true> : fwd_bf16_kernel<D, OUT_F32, false>;
+    // A build rotates keys in the forward or in the pack, never both (in the
+    // rotate-in-forward build every bf16 forward has a.k_table); that build
+    // runs no stream-K tail (its tail kernel would spill registers).
+    void (*kern)(FwdArgs);
+    if constexpr (SA_ROTATE_K_IN_FORWARD) {
+        if (!a.k_table || a.tail_units) return hipErrorInvalidValue;
+        kern = fwd_bf16_kernel<D, OUT_F32, true, false>;
+    } else {
+        if (a.k_table) return hipErrorInvalidValue;
+        kern = a.tail_units ? fwd_bf16_kernel<D, OUT_F32, false, true> : fwd_bf16_kernel<D, OUT_F32, false, false>;
+    }
     constexpr int lds_bytes = 3 * Tile<D, kNW>::BUF;
     // More than 64 KiB of dynamic LDS must be allowed explicitly (per device,
     // idempotent, no stream work).

@@ -1,7 +1,9 @@
-"""The balanced-tail forward (sa_forward_ws): the last, at most half-full round
-of (head, query tile) units runs as key halves merged by their log-sum-exps.
-Checked against the fp64 oracle and against the plain forward, which every
-unit outside the tail must match bit for bit."""
+"""The stream-K tail of the forward (sa_forward_ws): the units of a last round
+that would leave at least a quarter of the CUs idle are spread over all CUs
+as equal contiguous ranges of their key tiles, the units a range boundary
+cuts merged by their log-sum-exps. Checked against the fp64 oracle and
+against the plain forward, which every unit computed whole must match bit
+for bit."""
 
 import math
 
@@ -15,23 +17,35 @@ from streaming_video_diffusion_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-def plan(nq, heads):
-    """(units in the tail, first tail unit) as the library plans them on this GPU."""
+
+def plan(nq, heads, nk):
+    """(units in the tail, first tail unit, key tiles per unit) as the library
+    plans them on this GPU."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     units = math.ceil(nq / rows_per_workgroup()) * heads
     rounds = math.ceil(units / n_cu)
     r = units - (rounds - 1) * n_cu
-    if rounds < 2 or 2 * r > n_cu:
-        return 0, units
-    return r, units - r
+    ntiles = math.ceil(nk / 64)
+    if 4 * r > 3 * n_cu or r * ntiles < 4 * n_cu:
+        return 0, units, ntiles
+    return r, units - r, ntiles
 
 
-def tail_mask(nq, heads, first_unit):
-    """[nq][heads] True where the (row, head) belongs to a tail unit."""
+def whole_units(units, first_unit, ntiles):
+    """Tail units (counted from first_unit) that one workgroup's range holds
+    whole: computed exactly as by the plain forward."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    total = units * ntiles
+    wg = lambda x: ((x + 1) * n_cu - 1) // total  # noqa: E731
+    return [first_unit + u for u in range(units) if wg(u * ntiles) == wg((u + 1) * ntiles - 1)]
+
+
+def unit_mask(nq, heads, units):
+    """[nq][heads] True where the (row, head) belongs to one of ``units``."""
     BM = rows_per_workgroup()
     n_qt = math.ceil(nq / BM)
     m = np.zeros((nq, heads), dtype=bool)
-    for u in range(first_unit, n_qt * heads):
+    for u in units:
         h, qt = divmod(u, n_qt)
         m[qt * BM:min((qt + 1) * BM, nq), h] = True
     return m
@@ -40,30 +54,42 @@ def tail_mask(nq, heads, first_unit):
 def balanced_case():
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     heads = n_cu // 8            # 9 query tiles x n_cu/8 heads = n_cu + n_cu/8 units: a tail of n_cu/8
-    return I.custom("balanced", 600, "bf16", heads, 128, [150, 130], 9 * rows_per_workgroup() - 100, prompt_rows=20)
+    return I.custom("balanced", 600, "bf16", heads, 128, [1500, 1300], 9 * rows_per_workgroup() - 100,
+                    prompt_rows=20)
+
+
+def shard_case():
+    """One GPU's share of an 8-way head split of the 1344x768 chunk: 5 heads, 160 units on 256 CUs."""
+    import dataclasses
+    return dataclasses.replace(I.full_1344x768(), name="full_1344x768_h5", heads=5)
 
 
 def test_workspace_bytes_follow_the_rounds():
-    for w in (I.full_1344x768(), I.lowres_bf16(), balanced_case()):
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for w in (I.full_1344x768(), I.lowres_bf16(), balanced_case(), shard_case(), I.first_window_1344x768()):
         ctx = B.PackedContext(w.heads, w.head_dim, torch.bfloat16, w.nk)
         ctx.rows = w.nk
-        r, _ = plan(w.nq, w.heads)
-        assert B.sa_forward_workspace_bytes(ctx, w.nq) == 2 * r * rows_per_workgroup() * (w.head_dim + 1) * 4, w.name
+        r, _, _ = plan(w.nq, w.heads, w.nk)
+        want = 2 * n_cu * rows_per_workgroup() * (w.head_dim + 1) * 4 if r else 0
+        assert B.sa_forward_workspace_bytes(ctx, w.nq) == want, w.name
+    assert plan(shard_case().nq, 5, shard_case().nk)[0] == 160
+    assert plan(I.full_1344x768().nq, 40, I.full_1344x768().nk)[0] == 0   # 1280 units: five full rounds
 
 
 @pytest.mark.parametrize("out_dtype", [None, torch.float32], ids=["out_bf16", "out_f32"])
-def test_balanced_small_full(out_dtype):
+def test_tail_small_full(out_dtype):
     w = balanced_case()
-    r, first = plan(w.nq, w.heads)
+    r, first, ntiles = plan(w.nq, w.heads, w.nk)
     assert r > 0
     ca, out = run(w, out_dtype=out_dtype)
     assert ca.workspace is not None
     rel, mx = assert_parity(out, oracle(ca), "bf16", w.name)
-    note(f"  {w.name}: tail of {r} units, rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    note(f"  {w.name}: tail of {r} units x {ntiles} tiles, rel-L2 {rel:.3e} max-abs {mx:.3e}")
     plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale, out_dtype=ca.out_dtype)
     torch.cuda.synchronize()
-    keep = torch.from_numpy(~tail_mask(w.nq, w.heads, first)).cuda()
-    assert torch.equal(plain[keep], ca.out[keep]), "units outside the tail must match the plain forward"
+    same = list(range(first)) + whole_units(r, first, ntiles)
+    keep = torch.from_numpy(unit_mask(w.nq, w.heads, same)).cuda()
+    assert torch.equal(plain[keep], ca.out[keep]), "units computed whole must match the plain forward"
 
 
 def test_no_workspace_is_the_plain_forward():
@@ -85,10 +111,30 @@ def test_small_workspace_is_rejected():
     assert e.value.status == -5
 
 
-def test_balanced_full_size_tail_rows():
-    """1344x768: the tail is the last units (the last heads); sampled rows of every head."""
-    w = I.full_1344x768()
-    r, first = plan(w.nq, w.heads)
+def test_tail_head_shard_full_size():
+    """5 heads of the 1344x768 chunk: all 160 units go through the tail (no whole rounds)."""
+    w = shard_case()
+    r, first, ntiles = plan(w.nq, w.heads, w.nk)
+    assert (r, first) == (160, 0)
+    ca, out = run(w)
+    rows = sample_rows(w.nq, extra=24, seed=12)
+    rel, mx = assert_parity(out[rows], oracle(ca, rows=rows), "bf16", w.name)
+    note(f"  {w.name}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale).float().cpu().numpy()
+    torch.cuda.synchronize()
+    whole = whole_units(r, first, ntiles)
+    note(f"  {len(whole)} of {r} units whole")
+    m = unit_mask(w.nq, w.heads, whole)
+    assert np.array_equal(plain[m], out[m])
+    cut = ~m
+    rel2 = np.linalg.norm(plain[cut] - out[cut]) / np.linalg.norm(plain[cut])
+    assert rel2 < 5e-3, rel2
+
+
+def test_tail_first_window_sampled_rows():
+    """The 7-frame first window: 2960 units, a last round of 144 spread over every CU."""
+    w = I.first_window_1344x768()
+    r, first, ntiles = plan(w.nq, w.heads, w.nk)
     ca, out = run(w)
     note(f"  tail of {r} units from unit {first}")
     rows = sample_rows(w.nq, seed=11)
@@ -97,5 +143,5 @@ def test_balanced_full_size_tail_rows():
     if r:
         plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale).float().cpu().numpy()
         torch.cuda.synchronize()
-        m = tail_mask(w.nq, w.heads, first)
-        assert np.array_equal(plain[~m], out[~m])
+        m = unit_mask(w.nq, w.heads, list(range(first)) + whole_units(r, first, ntiles))
+        assert np.array_equal(plain[m], out[m])

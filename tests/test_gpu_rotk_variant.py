@@ -49,3 +49,38 @@ def test_variant_full_size_sampled_rows(variant):
     ca, out = run(w)
     rows = sample_rows(w.nq)
     assert_parity(out[rows], oracle(ca, rows=rows), "bf16", "full_1344x768 (rotate-in-forward)")
+
+
+# The default build's tests of the rarer paths, run again with the variant
+# loaded: peaked scores and underflowing rows take the second pass (which
+# reloads every tile and rotates it again), and split-KV stores per-run
+# partial outputs and log-sum-exps.
+import test_gpu_parity as P  # noqa: E402
+import test_gpu_split as S  # noqa: E402
+
+
+@pytest.mark.parametrize("c_log2", [0.5, 4.0], ids=["scale_x0.5", "scale_x4"])
+def test_variant_peaked_scores(variant, c_log2):
+    note(f"[gpu] rotate-in-forward build: peaked scores x{c_log2}")
+    P.test_rescaling_path_large_scores(c_log2)
+
+
+def test_variant_underflowing_rows(variant):
+    note("[gpu] rotate-in-forward build: underflowing rows")
+    P.test_second_pass_underflowing_rows()
+
+
+def test_variant_mixed_rows_keep_neighbours_bitwise(variant):
+    note("[gpu] rotate-in-forward build: mixed rows")
+    P.test_second_pass_mixed_rows_keep_neighbours_bitwise()
+
+
+@pytest.mark.parametrize("n_splits", [1, 5, 29])
+def test_variant_split_kv(variant, n_splits):
+    note(f"[gpu] rotate-in-forward build: split-KV x{n_splits}")
+    S.test_split_lowres(n_splits)
+
+
+def test_variant_split_second_pass(variant):
+    note("[gpu] rotate-in-forward build: split-KV with peaked scores")
+    S.test_split_second_pass()

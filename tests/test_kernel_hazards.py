@@ -21,19 +21,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf16.hip")
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "fwd_bf16.s"
+BUILDS = {"default": ((), 8),                          # head_dim 64/128 x bf16/f32 output x plain/stream-K tail
+          "rotate_k_in_forward": (BLD.ROTK_FLAGS, 4)}  # head_dim 64/128 x bf16/f32 output
+
+
+@pytest.mark.parametrize("build", sorted(BUILDS))
+def test_every_forward_instantiation_is_clean(build, tmp_path):
+    defs, n_kernels = BUILDS[build]
+    out = tmp_path / "fwd_bf16.s"
     flags = [f for f in BLD.FLAGS if f not in ("-fPIC", "-shared")]
-    cmd = [BLD.HIPCC, *flags, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    cmd = [BLD.HIPCC, *flags, *defs, "--cuda-device-only", "-S", SRC, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    return out.read_text()
-
-
-def test_every_forward_instantiation_is_clean(asm):
-    ks = {n: b for n, b in kernels(asm).items() if "fwd_bf16_kernel" in n}
-    assert len(ks) == 8   # head_dim 64/128 x bf16/f32 output x rotate-in-forward or not
+    ks = {n: b for n, b in kernels(out.read_text()).items() if "fwd_bf16_kernel" in n}
+    assert len(ks) == n_kernels, sorted(ks)
     for name, body in ks.items():
         assert body.count("v_mfma_f32_32x32x16_bf16") > 100, name
         assert scan(body) == [], name

@@ -1,5 +1,5 @@
-"""sa_forward_noalloc: the balanced forward with the library's own per-device
-scratch, against sa_forward_ws with a caller workspace (the same kernels and
+"""sa_forward_noalloc: the stream-K tail forward with the library's own
+per-device scratch, against sa_forward_ws with a caller workspace (the same kernels and
 launches, so the two must agree bit for bit) and against the fp64 oracle on
 sampled rows. Two calls in a row, the second on a smaller input, so the
 second meets the scratch as the first left it."""
@@ -7,35 +7,24 @@ second meets the scratch as the first left it."""
 import pytest
 import torch
 
-from gpu_util import assert_parity, note, oracle, run, sample_rows
+from gpu_util import assert_parity, note, oracle, rows_per_workgroup, run, sample_rows
 from streaming_video_diffusion_amd import binding as B
 from streaming_video_diffusion_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
 
-def rows_per_workgroup():
-    """Query rows per (head, query tile) unit of the bf16 forward, read off the
-    workspace the library asks for: n_cu + 1 heads of one query row make a
-    second round holding a single unit, whose two key halves take
-    2 * rows * (head_dim + 1) * 4 bytes."""
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    ctx = B.PackedContext(n_cu + 1, 128, torch.bfloat16, 128, device="cuda")
-    ctx.rows = 128
-    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * 129 * 4)
-
-
 def case(name, cfg, tiles, short):
     """48 heads x ``tiles`` query tiles (the last one ``short`` rows short)
-    over a ragged 577-key context."""
+    over a ragged 2820-key context (45 key tiles)."""
     bm = rows_per_workgroup()
-    return I.custom(name, cfg, "bf16", 48, 128, [300, 257], tiles * bm - short, prompt_rows=20)
+    return I.custom(name, cfg, "bf16", 48, 128, [1500, 1300], tiles * bm - short, prompt_rows=20)
 
 
 def noalloc_vs_ws(w, out_dtype):
     ca, _ = run(w, out_dtype=out_dtype)
     need = B.sa_forward_workspace_bytes(ca.ctx, w.nq)
-    note(f"  {w.name}: nq {w.nq}, balanced scratch {need} bytes")
+    note(f"  {w.name}: nq {w.nq}, tail scratch {need} bytes")
     assert 0 < need <= B.SA_NOALLOC_SCRATCH_BYTES
     got = torch.full_like(ca.out, float("nan"))
     B.sa_forward_noalloc(ca.ctx, ca.q, got, ca.q_table, w.scale)
