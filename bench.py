@@ -34,9 +34,9 @@ FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf
 # written). Valid only for the forward source these counters were taken on
 # (None: not taken on the current source).
 TRAFFIC = {
-    "source_sha256": "91a05cb5cd06bc3ae3823d7f27f9ffff96e91fcffb77af555a1bd656dd3fb1ac",
-    "fetch_kib": 467209.2,
-    "write_kib": 120962.1,
+    "source_sha256": "3e0ebbfbbd9ee62cf607a271f242264e1de805a34fa7952c57450bf04b72be1b",
+    "fetch_kib": 466618.3,
+    "write_kib": 120963.6,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

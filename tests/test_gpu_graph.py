@@ -2,7 +2,7 @@
 
 The library's calls allocate nothing, never synchronise and take the stream
 from the caller, so a chunk (rotary tables of the template, in-place pack of
-the dynamic rows, forward with the balanced last round) can be captured and
+the dynamic rows, forward with the stream-K tail where it applies) can be captured and
 replayed, as the pages do for their fixed shapes (StreamRender-H3 page,
 inference-acceleration section). Every replay, with eager work and
 synchronisation between replays, must give the eager result bit for bit.
@@ -18,11 +18,19 @@ from streaming_video_diffusion_amd.stream import ChunkAttention
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["lowres_bf16", "full_1344x768"])
+def _shard():
+    """One GPU's 5-head share of the 1344x768 chunk: its forward runs the stream-K tail."""
+    import dataclasses
+    return dataclasses.replace(I.full_1344x768(), name="full_1344x768_h5", heads=5)
+
+
+@pytest.mark.parametrize("name", ["lowres_bf16", "full_1344x768", "full_1344x768_h5"])
 def test_captured_chunk_replays_match_eager(name):
     note(f"[gpu] graph capture {name}")
-    w = I.CONFIGS[name]()
+    w = _shard() if name == "full_1344x768_h5" else I.CONFIGS[name]()
     ca = ChunkAttention(w)
+    if name == "full_1344x768_h5":
+        assert ca.workspace is not None, "the shard's forward should take the stream-K tail"
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
