@@ -68,7 +68,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="full_1344x768")
     p.add_argument("--cpu-rows", type=int, default=2560, help="query rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,25 +159,26 @@ def shard_measure(steps):
     stream = torch.cuda.current_stream()
     ca.pack_static(stream)
     ca.step(stream)
-    for _ in range(3):
-        ca.forward(stream)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        ca.forward(stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    ms = _time(lambda: ca.forward(stream), stream, steps)
     return {"heads": 5, "nq": w.nq, "nk": w.nk, "forward_ms": ms,
             "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12,
             "workgroups": -(-w.nq // bf16_rows_per_workgroup()) * w.heads}
 
 
-def _time(fn, stream, steps):
+def _time(fn, stream, steps, warm_s=0.2):
+    """Mean ms per call of ``fn`` over ``steps`` calls, after warming for at
+    least ``warm_s`` seconds: the shader clock drops while the GPU idles (as
+    it does while inputs are built on the host) and takes tens of ms under
+    load to come back."""
+    import time
     import torch
-    for _ in range(3):
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)

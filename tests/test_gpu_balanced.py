@@ -92,6 +92,24 @@ def test_tail_small_full(out_dtype):
     assert torch.equal(plain[keep], ca.out[keep]), "units computed whole must match the plain forward"
 
 
+def test_tail_d64_qknorm():
+    """The tail at head_dim 64 with per-head QK-norm: 3 query tiles x 96 heads = 288 units (a last round of 32)."""
+    import dataclasses
+    w = dataclasses.replace(I.custom("tail_d64_qkn", 601, "bf16", 96, 64, [1700, 1400], 3 * rows_per_workgroup() - 7,
+                                     prompt_rows=33), qk_norm="per_head")
+    r, first, ntiles = plan(w.nq, w.heads, w.nk)
+    assert r > 0
+    ca, out = run(w)
+    assert ca.workspace is not None
+    rows = sample_rows(w.nq, extra=24, seed=3)
+    rel, mx = assert_parity(out[rows], oracle(ca, rows=rows), "bf16", w.name)
+    note(f"  {w.name}: tail of {r} units x {ntiles} tiles, rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale, q_norm=ca.q_norm).float().cpu().numpy()
+    torch.cuda.synchronize()
+    m = unit_mask(w.nq, w.heads, list(range(first)) + whole_units(r, first, ntiles))
+    assert np.array_equal(plain[m], out[m])
+
+
 def test_no_workspace_is_the_plain_forward():
     w = balanced_case()
     ca, _ = run(w)
