@@ -196,7 +196,8 @@ def other_workloads(steps, skip):
     history + current as queries, the 7-frame first window, the prefix
     self-attention pass), and
     the 40 audio-only queries of the video+audio chunk run over 32 key splits
-    + merge vs one plain forward. Extra lines, not the metric."""
+    + merge, through the stream-K tail (sa_forward_ws), and as one plain
+    forward. Extra lines, not the metric."""
     import torch
     from streaming_video_diffusion_amd import binding as B
     from streaming_video_diffusion_amd import inputs as I
@@ -225,7 +226,12 @@ def other_workloads(steps, skip):
                 B.sa_combine_splits(part, lse, out=out, stream=stream)
 
             plain = _time(lambda: B.sa_forward(ca.ctx, q, qt, w.scale, out=out, stream=stream), stream, steps)
-            res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps)}
+            need = B.sa_forward_workspace_bytes(ca.ctx, 40)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
+            tail = _time(lambda: B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws),
+                         stream, steps)
+            res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps),
+                                             "stream_k_tail_ms": tail}
         del ca
         torch.cuda.empty_cache()
     res["tier_stream_1344x768"] = tier_stream_measure(steps)
