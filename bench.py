@@ -7,9 +7,10 @@ timing), and the forward pass. Inputs are resident in HBM before timing.
 
 Prints ONE JSON line. ``value`` is attention TFLOP/s over the whole step
 (4*Nq*Nk*d*H flops per chunk / step time); ``ms_per_step`` is ms per chunk.
-``roofline`` prices the forward (the dominant kernel: its launch over the
-balanced tail's key halves, its launch over the other units, and their merge)
-from HIP events around each forward in the timed region; ``cpu_baseline``
+``roofline`` prices the forward (the dominant kernel: one launch at 1344x768,
+whose 1280 units fill five rounds; where a stream-K tail applies, also its
+tail launch and merge) from HIP events around each forward in the timed
+region; ``cpu_baseline``
 times the fp64 oracle on a bounded sample of the same workload on the host
 cores.
 """

@@ -382,7 +382,7 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
 
 // The launches of a forward with a stream-K tail (a: validated arguments, p: a
 // plan with units > 0, workspace: device memory of at least tail_bytes(p)).
-static sa_status balanced_launch(const sa_context *ctx, const sa::FwdArgs &a, const TailPlan &p, void *workspace,
+static sa_status tail_launch(const sa_context *ctx, const sa::FwdArgs &a, const TailPlan &p, void *workspace,
                                  hipStream_t stream) {
     const int64_t nq = a.nq;
     const int64_t bm = sa::fwd_bf16_rows_per_workgroup();
@@ -436,7 +436,7 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
     if (workspace_bytes < need)
         return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    return balanced_launch(ctx, a, p, workspace, stream);
+    return tail_launch(ctx, a, p, workspace, stream);
 }
 
 // Device address of `scratch` per device, looked up once per device (with
@@ -483,8 +483,8 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
     st = scratch_address(&ws);
     if (st != SA_OK) return st;
     // Every word of the scratch a call reads is written earlier in the same
-    // call (the key halves, then the merge), so nothing needs clearing.
-    return balanced_launch(ctx, a, p, ws, stream);
+    // call (the tail's pieces, then the merge), so nothing needs clearing.
+    return tail_launch(ctx, a, p, ws, stream);
 }
 
 sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,

@@ -3,7 +3,7 @@
 The other full-size tests compare sampled rows (each exact, since rows are
 independent); these compare every one of the Nq x 40 x 128 outputs of the
 1344x768 chunk and of the hierarchical-history chunk, in the launch
-configuration the benchmark times (balanced last round). The oracle runs in
+configuration the benchmark times (sa_forward_ws). The oracle runs in
 float64 on the host cores, about a minute per workload.
 """
 
