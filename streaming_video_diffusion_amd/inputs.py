@@ -161,14 +161,18 @@ class Workload:
     def norm_weights(self):
         """QK-norm weights (query, key): float32 [d] or [H][d], drawn as
         1 + 0.2 N(0, 1); ``None`` when the workload has no QK-norm."""
-        if self.qk_norm is None:
-            return None
-        shape = (self.head_dim,) if self.qk_norm == "shared" else (self.heads, self.head_dim)
-        out = []
-        for tensor_id in (900, 901):
-            rng = np.random.default_rng(np.random.SeedSequence([ENTROPY, self.cfg_id, tensor_id]))
-            out.append((1.0 + 0.2 * rng.standard_normal(shape)).astype(np.float32))
-        return tuple(out)
+        return _norm_weights(self.cfg_id, self.heads, self.head_dim, self.qk_norm)
+
+
+def _norm_weights(cfg_id, heads, head_dim, kind):
+    if kind is None:
+        return None
+    shape = (head_dim,) if kind == "shared" else (heads, head_dim)
+    out = []
+    for tensor_id in (900, 901):
+        rng = np.random.default_rng(np.random.SeedSequence([ENTROPY, cfg_id, tensor_id]))
+        out.append((1.0 + 0.2 * rng.standard_normal(shape)).astype(np.float32))
+    return tuple(out)
 
 
 def _video_segments(prompt, grid_h, grid_w, ref_t, tiers, cur_t, audio=0, produce=False):
@@ -311,12 +315,18 @@ class TierStream:
     axis_dims: tuple = None
     scale: float = None
     description: str = ""
+    qk_norm: str = None         # None, "shared" ([d] weights) or "per_head" ([H][d] weights)
+    norm_eps: float = 1e-6
 
     def __post_init__(self):
         if self.axis_dims is None:
             self.axis_dims = AXIS_DIMS[self.head_dim]
         if self.scale is None:
             self.scale = 1.0 / math.sqrt(self.head_dim)
+
+    def norm_weights(self):
+        """QK-norm weights (query, key) as for ``Workload``, or ``None``."""
+        return _norm_weights(self.cfg_id, self.heads, self.head_dim, self.qk_norm)
 
     @property
     def chunk_rows(self):

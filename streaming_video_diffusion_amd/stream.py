@@ -145,10 +145,12 @@ class TierStreamAttention:
     position and writes it after the static rows, which are never touched
     again. The position template is fixed (reference at t = 0, the tiers
     oldest first, then the current chunk), so its rotary tables are built
-    once.
+    once. With QK-norm every key (prompt, reference, the tiers' means and
+    the current chunk) is normalised in the pack and every query in the
+    forward, before the rotation.
 
     ``stream`` is an ``inputs.TierStream`` (shapes, template positions,
-    static prompt / reference values).
+    static prompt / reference values, QK-norm weights).
     """
 
     # (pooling factor, age in chunks) of the history tiers, oldest first
@@ -162,6 +164,11 @@ class TierStreamAttention:
         self.dtype = torch.bfloat16 if st.dtype == "bf16" else torch.float32
         self.out_dtype = out_dtype or self.dtype
         rows = st.chunk_rows
+        self.q_norm = self.k_norm = None
+        weights = st.norm_weights()
+        if weights is not None:
+            qw, kw = (torch.from_numpy(x).to(dev) for x in weights)
+            self.q_norm, self.k_norm = B.Norm(qw, st.norm_eps), B.Norm(kw, st.norm_eps)
         self.static = []
         row = 0
         for k, v, pos in st.static_kv():
@@ -190,7 +197,8 @@ class TierStreamAttention:
     def pack_static(self, stream=None):
         """Pack the prompt and the reference frame (once per session and bank)."""
         self.ctx.rows = max(self.ctx.rows, self.static_rows)
-        B.sa_pack_context(self.ctx, [(k, v, dst, table) for k, v, dst, table in self.static], stream=stream)
+        B.sa_pack_context(self.ctx, [(k, v, dst, table, self.k_norm) for k, v, dst, table in self.static],
+                          stream=stream)
 
     def tiers(self):
         """``[(pool, chunk index, k, v)]`` of the history of the current
@@ -223,9 +231,9 @@ class TierStreamAttention:
         for s, _, tk, tv in self.tiers():
             slot = [t for t, _ in self.TIERS].index(s)
             pool = (s, st.grid_h, st.grid_w) if s > 1 else None
-            segs.append((tk, tv, row, self.tier_tables[slot], None, pool))
+            segs.append((tk, tv, row, self.tier_tables[slot], self.k_norm, pool))
             row += tk.shape[0] // (s * s)
-        segs.append((k, v, row, self.q_table))
+        segs.append((k, v, row, self.q_table, self.k_norm))
         row += k.shape[0]
         self.ctx.rows = row
         B.sa_pack_context(self.ctx, segs, stream=stream)
@@ -235,6 +243,6 @@ class TierStreamAttention:
         ws = B.sa_forward_workspace_bytes(self.ctx, q.shape[0])
         if ws and (self.workspace is None or self.workspace.numel() < ws):
             self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
-        B.sa_forward_ws(self.ctx, q, self.q_table, self.st.scale, out=self.out, stream=stream,
+        B.sa_forward_ws(self.ctx, q, self.q_table, self.st.scale, out=self.out, stream=stream, q_norm=self.q_norm,
                         workspace=self.workspace if ws else None)
         return self.out

@@ -42,9 +42,11 @@ def _run(stream, chunks, rows_of=None):
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
         rows = None if rows_of is None else rows_of(c)
+        weights = stream.norm_weights()
+        qn, kn = (None, None) if weights is None else ((weights[0], stream.norm_eps), (weights[1], stream.norm_eps))
         want = tiers64.chunk_attention(q, stream.slot_positions(len(ts.TIERS)), static, stream.chunk_kv, c,
                                        stream.frames, stream.grid_h, stream.grid_w, stream.axis_dims, stream.theta,
-                                       stream.scale, rows=rows)
+                                       stream.scale, rows=rows, q_norm=qn, k_norm=kn)
         rel, mx = assert_parity(got if rows is None else got[rows], want, stream.dtype, f"{stream.name} chunk {c}")
         note(f"  chunk {c}: nk {ts.ctx.rows} rel-L2 {rel:.3e} max-abs {mx:.3e}")
         expect_nk = n_static + sum(stream.chunk_rows // (s * s) for s, age in ts.TIERS if c - age >= 0) + stream.chunk_rows
@@ -66,6 +68,12 @@ def _run(stream, chunks, rows_of=None):
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_tier_stream_small_every_chunk(dtype, d):
     _run(I.tier_stream_small(dtype, d), 6)
+
+
+@pytest.mark.parametrize("kind", ["shared", "per_head"])
+def test_tier_stream_small_qknorm(kind):
+    import dataclasses
+    _run(dataclasses.replace(I.tier_stream_small("bf16", 128), name=f"tier_stream_small_qkn_{kind}", qk_norm=kind), 5)
 
 
 def test_tier_stream_1344x768_sampled():
