@@ -61,27 +61,40 @@ constexpr int kBM = kNW * kQB * 32;  // queries per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
+// 16-byte operand read at an LDS byte address.
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
     return *reinterpret_cast<lds_bf16x8 *>((uintptr_t)addr);
 }
 
+// Physical 16-byte chunk of a tile row: XOR swizzles that keep the matrix-core
+// operand reads (32 rows, one logical chunk) free of LDS bank conflicts for
+// 32 or 64 banks. A 256-byte row swizzles by its low 4 row bits; a 128-byte
+// row (two rows per 64 banks) by ((r >> 1) & 7) ^ ((r & 1) << 2).
 __device__ __forceinline__ int swz256(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz128(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
 
 template <int D, int NW>
 struct Tile {
-    static constexpr int KROW = D * 2;
-    static constexpr int VROW = BN * 2;
+    static constexpr int KROW = D * 2;            // bytes per K row
+    static constexpr int VROW = BN * 2;           // bytes per V^T row (128)
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = D * VROW;
-    static constexpr int BUF = KBYTES + VBYTES;
-    static constexpr int KINSTR = KBYTES / 1024;
+    static constexpr int BUF = KBYTES + VBYTES;   // bytes per buffer
+    static constexpr int KINSTR = KBYTES / 1024;  // 1 KiB per wave-wide direct load
     static constexpr int VINSTR = VBYTES / 1024;
     static constexpr int KROWS_PER_INSTR = 1024 / KROW;
     static constexpr int VROWS_PER_INSTR = 1024 / VROW;
     static_assert(KINSTR % NW == 0 && VINSTR % NW == 0, "tile loads must split evenly over the waves");
 
     __device__ static __forceinline__ int kswz(int r, int c) { return D == 128 ? swz256(r, c) : swz128(r, c); }
+    // Operand-read addresses. For a lane reading row r (K) or d-row r (V^T),
+    // the physical chunk is (logical chunk) ^ key(r) with key depending only
+    // on r mod 16, and the XORed bits (5..7) are disjoint from the row and
+    // buffer bits. So every read address of a tile is a per-lane base plus
+    // the buffer offset, XORed with a constant, plus an immediate offset:
+    //   K   row 32 h + l32, chunk 2 j + hf:  ((A0 + buf) ^ 32 j) + h * 32 * KROW
+    //   V^T row 32 c + l32, chunk 4 h + 2 g + hf:  ((B0 + buf) ^ (64 h + 32 g)) + c * 32 * VROW
+    // A0 and B0 are the only per-lane address registers kept live.
     __device__ static __forceinline__ uint32_t kbase(int l32, int hf) {
         const int key = D == 128 ? (l32 & 15) : swz128(l32, 0);
         return (uint32_t)(l32 * KROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
@@ -90,8 +103,13 @@ struct Tile {
         const int key = swz128(l32, 0);
         return (uint32_t)(KBYTES + l32 * VROW + 16 * (key & ~1) + 16 * ((hf ^ key) & 1));
     }
+    // byte offset of logical chunk c of K row r inside a buffer
     __device__ static __forceinline__ int koff(int r, int c) { return r * KROW + kswz(r, c) * 16; }
 
+    // Loop-invariant per-lane byte offsets of this wave's share of one tile's
+    // direct global->LDS loads (K relative to the tile's first K row, V^T
+    // relative to the tile's first V^T column), so each tile only moves a
+    // wave-uniform base offset.
     struct Plan {
         uint32_t k[KINSTR / NW];
         uint32_t v[VINSTR / NW];
@@ -112,6 +130,15 @@ struct Tile {
         }
         return pl;
     }
+    // Issue this wave's share of the direct buffer->LDS loads of one K/V^T
+    // tile: the loop-invariant lane offsets plus the tile's wave-uniform byte
+    // offset (a scalar operand). kr / vr describe one head's packed K / V^T
+    // (below 2^31 bytes each). The packed capacity is a multiple of the tile,
+    // so the last tile never leaves the allocation; its rows past nk hold
+    // zeros written by the pack step, and their scores are masked. (Buffer
+    // rather than global loads: with a global load to LDS in flight the
+    // compiler can only wait for all LDS reads at once, which would undo the
+    // read-ahead of the operand reads.)
     __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, __amdgpu_buffer_rsrc_t kr,
                                                  __amdgpu_buffer_rsrc_t vr, uint32_t k0, int w) {
 #pragma unroll
@@ -127,6 +154,7 @@ struct Tile {
 
 __device__ __forceinline__ void vm_lgkm_cnt0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
+// Value of lane l ^ 32 (the other half-wave holds the same query column).
 __device__ __forceinline__ float half_swap_partner(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -317,6 +345,9 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
         vm_lgkm_cnt0();
         __syncthreads();
     };
+    // Rotate-in-forward build: the workgroup rotates the landed (unrotated)
+    // keys of tile kt_r in place in LDS with their per-row tables, then meets
+    // a barrier that waits for LDS only.
     auto rotate_k = [&](int kt_r) __attribute__((always_inline)) {
         if (kt_r < ntiles) {
             unsigned char *bb = buf_of(kt_r);
@@ -415,6 +446,12 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
     constexpr int LV = 3;
     constexpr int EOFF = 2;  // first exponential two slots into the stage
 
+    // One pipeline stage. pv: P of unit i (B operand of its P.V products, from
+    // V^T tile vb, key half vhalf). QK: also form sw = S of unit i + 2 from the
+    // K unit at kb (KPRE: its first LK operands are in kpre, read by the
+    // previous stage). EX: exponentiate sr = S of unit i + 1 into pw (and add
+    // its row sums). NXK / NXV: read the next stage's first K operands (unit
+    // at nkb) into kpre / V^T operands (tile nvb, half nvhalf) into vpre.
     auto stage = [&](auto QK_, auto EX_, auto KPRE_, auto NXK_, auto NXV_, uint32_t kb, uint32_t nkb, uint32_t vb,
                      int vhalf, uint32_t nvb, int nvhalf, f32x16 (&sw)[QB], f32x16 (&sr)[QB],
                      const bf16x8 (&pv)[QB][2], bf16x8 (&pw)[QB][2], bf16x8 (&kpre)[LK], bf16x8 (&vpre)[LV])
