@@ -110,6 +110,23 @@ def test_tail_d64_qknorm():
     assert np.array_equal(plain[m], out[m])
 
 
+def test_tail_strided_output_view():
+    """The tail's merge writes through the caller's row and head strides: a
+    view into a wider buffer gets exactly the contiguous result, and nothing
+    outside the view changes."""
+    w = balanced_case()
+    ca, _ = run(w)
+    want = ca.out.clone()
+    big = torch.full((w.nq, w.heads + 3, w.head_dim + 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, 1:1 + w.heads, 32:32 + w.head_dim]
+    B.sa_forward_ws(ca.ctx, ca.q, ca.q_table, w.scale, out=view, workspace=ca.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(view, want)
+    outside = torch.ones_like(big, dtype=torch.bool)
+    outside[:, 1:1 + w.heads, 32:32 + w.head_dim] = False
+    assert bool((big[outside] == 7.0).all())
+
+
 def test_no_workspace_is_the_plain_forward():
     w = balanced_case()
     ca, _ = run(w)
