@@ -127,6 +127,22 @@ def test_tail_strided_output_view():
     assert bool((big[outside] == 7.0).all())
 
 
+def test_tail_one_query_row():
+    """150 heads of one query row: every unit is a single valid row (the rest
+    of its 384 are padding the merge must skip), all in the tail."""
+    w = I.custom("tail_one_row", 602, "bf16", 150, 128, [1700, 1300], 1, prompt_rows=11)
+    r, first, ntiles = plan(w.nq, w.heads, w.nk)
+    assert (r, first) == (150, 0)
+    ca, out = run(w)
+    assert ca.workspace is not None
+    rel, mx = assert_parity(out, oracle(ca), "bf16", w.name)
+    note(f"  {w.name}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    plain = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale).float().cpu().numpy()
+    torch.cuda.synchronize()
+    m = unit_mask(w.nq, w.heads, whole_units(r, first, ntiles))
+    assert np.array_equal(plain[m], out[m])
+
+
 def test_no_workspace_is_the_plain_forward():
     w = balanced_case()
     ca, _ = run(w)
