@@ -51,3 +51,31 @@ def test_noalloc_without_a_tail_is_the_plain_forward():
     want = B.sa_forward(ca.ctx, ca.q, ca.q_table, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+def test_noalloc_forward_captured_and_replayed():
+    """The callers it is for: a forward captured into a HIP graph (after one
+    eager call, which looks up the scratch's device address) and replayed,
+    each replay bitwise equal to the eager result, with eager work between."""
+    w = case("noalloc_graph", 613, 7, 60)
+    ca, _ = run(w)
+    eager = torch.empty_like(ca.out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.sa_forward_noalloc(ca.ctx, ca.q, eager, ca.q_table, w.scale, stream=side)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ca.out)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        B.sa_forward_noalloc(ca.ctx, ca.q, out, ca.q_table, w.scale, stream=side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        other = B.sa_forward_noalloc(ca.ctx, ca.q[: ca.q.shape[0] // 2], torch.empty_like(ca.out[: ca.q.shape[0] // 2]),
+                                     ca.q_table[: ca.q.shape[0] // 2], w.scale)   # eager work on the same scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del other
