@@ -76,34 +76,47 @@ hipError_t launch_t(const CombineArgs &a, hipStream_t stream) {
 // i0 = i(ul T) .. i1 = i((ul + 1) T - 1) with a non-empty range, in slot 2i
 // when the unit is the first of that range, else 2i + 1. Row r of the unit is
 // query row qt * bm + r of its head; rows past nq are padding.
+// A block holds RPB rows of one unit (bm is a multiple of RPB): its first
+// thread lists the unit's piece slots in LDS once, so the 64-bit index
+// arithmetic is not repeated per row.
+constexpr int kMaxPieces = 1024;  // pieces of one unit: at most G / units + 2 (G <= 1022 CUs)
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void tail_combine_kernel(TailCombineArgs a) {
     constexpr int LPR = D / 4;
     constexpr int RPB = kThreads / LPR;
-    const int64_t ur = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;  // unit * bm + row
-    const int c = (threadIdx.x % LPR) * 4;
-    if (ur >= (int64_t)a.units * a.bm) return;
-    const int ul = (int)(ur / a.bm);
-    const int r = (int)(ur - (int64_t)ul * a.bm);
+    __shared__ int slots[kMaxPieces];
+    __shared__ int n_pieces;
+    const int blocks_per_unit = a.bm / RPB;
+    const int ul = (int)(blockIdx.x / blocks_per_unit);
+    const int r = (int)(blockIdx.x - ul * blocks_per_unit) * RPB + (int)threadIdx.x / LPR;
+    const int c = ((int)threadIdx.x % LPR) * 4;
+    if (threadIdx.x == 0) {
+        const int64_t T = a.ntiles, G = a.wgs, total = (int64_t)a.units * T;
+        const int64_t x0 = (int64_t)ul * T, x1 = x0 + T - 1;
+        const int i0 = (int)(((x0 + 1) * G - 1) / total), i1 = (int)(((x1 + 1) * G - 1) / total);
+        int n = 0;
+        if (i0 != i1) {  // else stored whole by workgroup i0
+            for (int i = i0; i <= i1 && n < kMaxPieces; ++i) {
+                const int64_t bi = (int64_t)i * total / G;
+                if ((int64_t)(i + 1) * total / G > bi) slots[n++] = bi / T == ul ? 2 * i : 2 * i + 1;
+            }
+        }
+        n_pieces = n;
+    }
+    __syncthreads();
+    const int n = n_pieces;
     const int u = a.first_unit + ul;
     const int head = u / a.n_qt;
     const int qt = u - head * a.n_qt;
     const int64_t row = (int64_t)qt * a.bm + r;
-    if (row >= a.nq) return;
-    const int64_t T = a.ntiles, G = a.wgs, total = (int64_t)a.units * T;
-    const int64_t x0 = (int64_t)ul * T, x1 = x0 + T - 1;
-    const int i0 = (int)(((x0 + 1) * G - 1) / total), i1 = (int)(((x1 + 1) * G - 1) / total);
-    if (i0 == i1) return;  // stored whole by workgroup i0
-    auto slot_of = [&](int i) { return (i * total / G) / T == ul ? 2 * i : 2 * i + 1; };
-    auto nonempty = [&](int i) { return (int64_t)(i + 1) * total / G > (int64_t)i * total / G; };
+    if (n == 0 || row >= a.nq) return;
     float mx = -__builtin_inff();
-    for (int i = i0; i <= i1; ++i)
-        if (nonempty(i)) mx = fmaxf(mx, a.lse[(int64_t)slot_of(i) * a.bm + r]);
+    for (int k = 0; k < n; ++k) mx = fmaxf(mx, a.lse[(int64_t)slots[k] * a.bm + r]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int i = i0; i <= i1; ++i) {
-        if (!nonempty(i)) continue;
-        const int64_t pr = (int64_t)slot_of(i) * a.bm + r;
+    for (int k = 0; k < n; ++k) {
+        const int64_t pr = (int64_t)slots[k] * a.bm + r;
         const float wgt = expf(a.lse[pr] - mx);
         wsum += wgt;
         const f32x4 p = *reinterpret_cast<const f32x4 *>(a.part + pr * D + c);
@@ -120,8 +133,8 @@ __global__ __launch_bounds__(kThreads) void tail_combine_kernel(TailCombineArgs 
 template <int D, bool OUT_F32>
 hipError_t launch_tail_t(const TailCombineArgs &a, hipStream_t stream) {
     constexpr int RPB = kThreads / (D / 4);
-    const int64_t rows = (int64_t)a.units * a.bm;
-    const int64_t blocks = (rows + RPB - 1) / RPB;
+    if (a.bm % RPB != 0 || a.wgs + 2 > kMaxPieces) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)a.units * (a.bm / RPB);
     hipLaunchKernelGGL((tail_combine_kernel<D, OUT_F32>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
