@@ -353,8 +353,8 @@ def sa_forward_workspace_bytes(ctx, nq):
 def sa_forward_ws(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=None, stream=None, q_norm=None,
                   workspace=None):
     """``sa_forward`` with a device workspace (a tensor of at least
-    ``sa_forward_workspace_bytes`` bytes, or None) that balances the last
-    round of workgroups."""
+    ``sa_forward_workspace_bytes`` bytes, or None) that lets a part-empty
+    last round of workgroups spread over every CU (the stream-K tail)."""
     _check_query(ctx, q, q_rope, q_norm)
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:

@@ -70,7 +70,7 @@ class ChunkAttention:
         self.ctx = B.PackedContext(w.heads, w.head_dim, self.dtype, w.nk, device=dev)
         self.ctx.rows = w.nk
         self.out = torch.empty((w.nq, w.heads, w.head_dim), dtype=self.out_dtype, device=dev)
-        # Workspace that lets the forward balance its last round of workgroups
+        # Workspace that lets a part-empty last round of workgroups spread over every CU
         # (allocated once; None when the forward would not use it).
         ws = B.sa_forward_workspace_bytes(self.ctx, w.nq)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
