@@ -31,22 +31,40 @@ constexpr int kThreads = 256;
 // group; perm swaps 4..7 with 8..11 and is its own inverse.
 __device__ __forceinline__ int group_perm(int j) { return (j & 3) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
+// The E QK-norm weights of the elements c0 .. c0 + E - 1 of head h's rows
+// (all ones without a weight), loaded once per work unit.
+template <int E>
+__device__ __forceinline__ void norm_weights(const NormArgs &n, int h, int d, int c0, float (&w)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = 1.0f;
+    if (!n.on || !n.weight) return;
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(n.weight + (n.per_head ? (int64_t)h * d : 0) + c0);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+        const f32x4 v = p[q];
+        w[4 * q] = v.x;
+        w[4 * q + 1] = v.y;
+        w[4 * q + 2] = v.z;
+        w[4 * q + 3] = v.w;
+    }
+}
+
 // RMS normalisation of one key row held by CH consecutive lanes, E elements
-// per lane starting at element c0 of the row (QK-norm, applied before the
-// rotation): the row's mean square is summed across those lanes in float32.
-// Every lane of a CH-lane group is active or inactive together (one row per
-// group), so the exchange stays within active lanes.
+// per lane (QK-norm, applied before the rotation): the row's mean square is
+// summed across those lanes in float32, then each element is scaled by the
+// reciprocal root and its weight w. Every lane of a CH-lane group is active
+// or inactive together (one row per group), so the exchange stays within
+// active lanes.
 template <int CH, int E>
-__device__ __forceinline__ void norm_row(float (&x)[E], const NormArgs &n, int h, int d, int c0) {
+__device__ __forceinline__ void norm_row(float (&x)[E], float eps, int d, const float (&w)[E]) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
 #pragma unroll
     for (int m = 1; m < CH; m <<= 1) ss += __shfl_xor(ss, m);
-    const float r = 1.0f / __builtin_sqrtf(ss / (float)d + n.eps);
-    const float *w = n.weight ? n.weight + (n.per_head ? (int64_t)h * d : 0) + c0 : nullptr;
+    const float r = 1.0f / __builtin_sqrtf(ss / (float)d + eps);
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = x[e] * r * (w ? w[e] : 1.0f);
+    for (int e = 0; e < E; ++e) x[e] = x[e] * r * w[e];
 }
 
 // Spatial mean behind pooled row sr of a pooled segment (pool = P > 1): the
@@ -167,6 +185,8 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
     bf16 *vp = reinterpret_cast<bf16 *>(a.v_packed) + ((int64_t)h * D) * a.cap;
     const bf16 *ks = reinterpret_cast<const bf16 *>(s.k);
     const bf16 *vs = reinterpret_cast<const bf16 *>(s.v);
+    float nw[8];
+    norm_weights<8>(s.norm, h, D, chunk * 8, nw);
 
 #pragma unroll
     for (int p = 0; p < kPackTileRows / RPP; ++p) {
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(PackArgs a) {
             for (int e = 0; e < 8; ++e) x[e] = (float)kraw[e];
             vv = *reinterpret_cast<const bf16x8 *>(vs + sr * s.v_rs + h * s.v_hs + chunk * 8);
         }
-        if (s.norm.on) norm_row<CH, 8>(x, s.norm, h, D, chunk * 8);
+        if (s.norm.on) norm_row<CH, 8>(x, s.norm.eps, D, nw);
         if (a.k_table) {
             // keys stay unrotated; head 0's workgroup records the row's table
             // entries for this chunk's 4 pairs (identity without rotation)
@@ -277,6 +297,8 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
     float *vp = reinterpret_cast<float *>(a.v_packed) + ((int64_t)h * a.cap) * D;
     const float *ks = reinterpret_cast<const float *>(s.k);
     const float *vs = reinterpret_cast<const float *>(s.v);
+    float nw[4];
+    norm_weights<4>(s.norm, h, D, chunk * 4, nw);
 #pragma unroll
     for (int p = 0; p < kPackTileRows / RPP; ++p) {
         const int64_t row = r.tile_start + t / CH + p * RPP;
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void pack_f32_kernel(PackArgs a) {
         }
         if (s.norm.on) {
             float x[4] = {kv.x, kv.y, kv.z, kv.w};
-            norm_row<CH, 4>(x, s.norm, h, D, chunk * 4);
+            norm_row<CH, 4>(x, s.norm.eps, D, nw);
             kv = f32x4{x[0], x[1], x[2], x[3]};
         }
         if (s.rope) {
