@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s + ms/chunk at 1344x768 (12096 q x 28480 kv, 40 heads)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (published)
+HBM_PEAK_BPS = 8.0e12       # MI355X HBM3E bandwidth (published)
 FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf16.hip")
 # HBM traffic of one forward at 1344x768, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (KiB per forward; profiles/fwd_bf16_1344x768_hbm_traffic.txt),
@@ -45,15 +46,16 @@ TRAFFIC = {
 
 def bf16_rows_per_workgroup():
     """Query rows per (head, query tile) unit of the bf16 forward, read off the
-    workspace the library asks for: n_cu / 2 heads of one query row over 16 key
-    tiles make one part-empty round of n_cu / 2 units, which the stream-K tail
-    spreads over every CU, with 2 * n_cu slots of rows * (head_dim + 1) floats."""
+    workspace the library asks for: n_cu / 2 heads of SA_FEW_QUERY_ROWS + 1
+    query rows (one more than the few-query path takes) over 16 key tiles make
+    one part-empty round of n_cu / 2 units, which the stream-K tail spreads over
+    every CU, with 2 * n_cu slots of rows * (head_dim + 1) floats."""
     import torch
     from streaming_video_diffusion_amd import binding as B
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     ctx = B.PackedContext(n_cu // 2, 128, torch.bfloat16, 1024, device="cuda")
     ctx.rows = 1024
-    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * n_cu * 129 * 4)
+    return B.sa_forward_workspace_bytes(ctx, B.SA_FEW_QUERY_ROWS + 1) // (2 * n_cu * 129 * 4)
 
 
 def fwd_kernel_name(ca):
@@ -197,8 +199,9 @@ def other_workloads(steps, skip):
     history + current as queries, the 7-frame first window, the prefix
     self-attention pass), and
     the 40 audio-only queries of the video+audio chunk run over 32 key splits
-    + merge, through the stream-K tail (sa_forward_ws), and as one plain
-    forward. Extra lines, not the metric."""
+    + merge, through the few-query path (sa_forward_ws: key runs per wave +
+    merge, with its HBM rate over the K/V, Q and output bytes), and as one
+    plain forward. Extra lines, not the metric."""
     import torch
     from streaming_video_diffusion_amd import binding as B
     from streaming_video_diffusion_amd import inputs as I
@@ -229,10 +232,13 @@ def other_workloads(steps, skip):
             plain = _time(lambda: B.sa_forward(ca.ctx, q, qt, w.scale, out=out, stream=stream), stream, steps)
             need = B.sa_forward_workspace_bytes(ca.ctx, 40)
             ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
-            tail = _time(lambda: B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws),
+            fewq = _time(lambda: B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws),
                          stream, steps)
+            nbytes = w.nk * w.heads * w.head_dim * 2 * 2 + 2 * 40 * w.heads * w.head_dim * 2
             res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps),
-                                             "stream_k_tail_ms": tail}
+                                             "few_query_ms": fewq, "few_query_bytes": nbytes,
+                                             "few_query_tb_per_s": nbytes / (fewq * 1e-3) / 1e12,
+                                             "few_query_hbm_frac": nbytes / (fewq * 1e-3) / HBM_PEAK_BPS}
         del ca
         torch.cuda.empty_cache()
     res["tier_stream_1344x768"] = tier_stream_measure(steps)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 
 /* Packed context capacity (rows) must be a multiple of this (one key tile). */
 #define SA_ROW_ALIGN 64
@@ -59,11 +59,14 @@ extern "C" {
 #define SA_MAX_SEGMENTS 16
 /* Most key splits of sa_forward_split / sa_combine_splits. */
 #define SA_MAX_SPLITS 256
+/* Most query rows of the few-query path of sa_forward_ws / sa_forward_noalloc
+ * (bf16 contexts). */
+#define SA_FEW_QUERY_ROWS 64
 /* Largest spatial pooling factor of a segment (sa_segment.pool). */
 #define SA_MAX_POOL 8
 /* Bytes of device scratch sa_forward_noalloc holds on each device it runs on
  * (128 MiB: the stream-K tail needs at most 101.4 MB at head_dim 128 on 256
- * compute units). */
+ * compute units; a few-query plan is used only when it fits). */
 #define SA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef int32_t sa_status;
@@ -305,6 +308,15 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
  * workspace and the pieces merged by their log-sum-exps (the identity
  * sa_forward_split rests on), the other units run as usual. Same result as
  * sa_forward up to rounding, in fewer rounds.
+ *
+ * A bf16 forward of 1 <= nq <= SA_FEW_QUERY_ROWS query rows (the 40
+ * audio-only queries of a joint chunk: MiniMax-H3 deep-dive page, components
+ * table and DiT paragraph) takes the few-query path instead: every wave of a
+ * key-split kernel streams its own equal run of the head's key tiles for all
+ * nq rows, S = n_cu / heads workgroups of four waves per head (at least 1, at
+ * most a quarter of the key tiles), each run stored as its normalised float32
+ * output and log-sum-exp and the runs merged as sa_combine_splits merges them.
+ * It reads the packed K/V once and fills the chip however few the rows are.
  * workspace: device, 16-byte aligned, at least sa_forward_workspace_bytes()
  *            bytes for this context and nq on the current device; NULL (or a
  *            forward that gains nothing) runs exactly sa_forward. Calls that
@@ -321,11 +333,11 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
  * sa_forward_noalloc -- sa_forward_ws for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc. It computes exactly what sa_forward_ws computes with a
- * large enough workspace (same kernels, same launches), but the stream-K
- * tail's scratch is a device array the library holds, SA_NOALLOC_SCRATCH_BYTES
- * on every device it runs on, from that device's first call until the process
- * ends. The call itself allocates nothing; the caller passes inputs and
- * output as for sa_forward.
+ * large enough workspace (same kernels, same launches), but the scratch of
+ * the stream-K tail or the few-query path is a device array the library
+ * holds, SA_NOALLOC_SCRATCH_BYTES on every device it runs on, from that
+ * device's first call until the process ends. The call itself allocates
+ * nothing; the caller passes inputs and output as for sa_forward.
  * Every call on one device shares that device's scratch, and a call leaves
  * its partial results there: calls that may overlap on one device (other
  * streams, other threads, replays of graphs holding it) race and must be
@@ -345,7 +357,10 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
  * serves) bytes of workspace sa_forward_ws uses for this
  * context and nq on the current device (0 when it would run as sa_forward):
  * 2 * n_cu * 384 * (head_dim + 1) * 4 when the stream-K tail is used (101.4 MB
- * at head_dim 128 on 256 CUs).
+ * at head_dim 128 on 256 CUs); 4 S * nq * heads * (head_dim + 1) * 4 on the
+ * few-query path (S workgroups per head as above; 9.9 MB for 40 rows of 40
+ * heads at head_dim 128 on 256 CUs). A few-query plan that would need more than
+ * SA_NOALLOC_SCRATCH_BYTES is not used (such a forward takes the other paths).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, and the context checks of sa_forward.
  */
 sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes);

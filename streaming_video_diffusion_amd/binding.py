@@ -23,6 +23,7 @@ SA_ROW_ALIGN = 64
 SA_MAX_SEGMENTS = 16
 SA_NOALLOC_SCRATCH_BYTES = 128 << 20  # device scratch sa_forward_noalloc holds per device
 SA_MAX_SPLITS = 256
+SA_FEW_QUERY_ROWS = 64  # most query rows of the few-query path of sa_forward_ws / sa_forward_noalloc
 
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
 _TORCH = {SA_F32: torch.float32, SA_BF16: torch.bfloat16}
@@ -354,7 +355,9 @@ def sa_forward_ws(ctx, q, q_rope=None, softmax_scale=None, out=None, out_dtype=N
                   workspace=None):
     """``sa_forward`` with a device workspace (a tensor of at least
     ``sa_forward_workspace_bytes`` bytes, or None) that lets a part-empty
-    last round of workgroups spread over every CU (the stream-K tail)."""
+    last round of workgroups spread over every CU (the stream-K tail), and
+    bf16 forwards of at most ``SA_FEW_QUERY_ROWS`` query rows split their keys
+    over every wave of the chip (the few-query path)."""
     _check_query(ctx, q, q_rope, q_norm)
     qrs, qhs = _rows_heads(q, "q")
     if softmax_scale is None:

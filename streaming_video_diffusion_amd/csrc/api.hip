@@ -368,6 +368,65 @@ static size_t tail_bytes(const TailPlan &p, int head_dim) {
     return (size_t)2 * p.wgs * (size_t)sa::fwd_bf16_rows_per_workgroup() * (size_t)(head_dim + 1) * sizeof(float);
 }
 
+// Few-query plan of the bf16 forward: for 1 <= nq <= kFewqMaxRows every wave
+// of the few-query kernel streams its own run of key tiles for all the
+// queries of a head, S workgroups (4 S runs) per head, S = n_cu / heads so
+// that one round fills the chip (at least 1, and at most a quarter of the key
+// tiles so that no run is empty). The runs' partial outputs take
+// 4 S * nq * heads * (head_dim + 1) float32 values of workspace; a plan that
+// would need more than SA_NOALLOC_SCRATCH_BYTES is not used, so that
+// sa_forward_noalloc and sa_forward_ws run the same launches.
+struct FewqPlan {
+    int splits = 0;  // workgroups per head (0: not used)
+    size_t bytes = 0;
+};
+static FewqPlan fewq_plan(const sa_context *ctx, int64_t nq) {
+    FewqPlan p;
+    if (SA_ROTATE_K_IN_FORWARD || ctx->dtype != SA_BF16 || nq < 1 || nq > sa::kFewqMaxRows) return p;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return p;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0) return p;
+    const int64_t ntiles = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN;
+    int64_t s = n_cu / ctx->heads;
+    if (s > ntiles / sa::kFewqWaves) s = ntiles / sa::kFewqWaves;
+    if (s < 1) s = 1;
+    const size_t bytes =
+        (size_t)sa::kFewqWaves * s * (size_t)nq * ctx->heads * (size_t)(ctx->head_dim + 1) * sizeof(float);
+    if (bytes > (size_t)SA_NOALLOC_SCRATCH_BYTES) return p;
+    p.splits = (int)s;
+    p.bytes = bytes;
+    return p;
+}
+
+// The launches of a few-query forward (a: validated arguments, p: a plan with
+// splits > 0, workspace: device memory of at least p.bytes): every run's
+// partial output and log-sum-exp, then their merge into out.
+static sa_status fewq_launch(const sa_context *ctx, const sa::FwdArgs &a, const FewqPlan &p, void *workspace,
+                             hipStream_t stream) {
+    const int32_t runs = sa::kFewqWaves * p.splits;
+    float *part = static_cast<float *>(workspace);
+    float *lse = part + (size_t)runs * a.nq * ctx->heads * ctx->head_dim;
+    sa::FwdArgs f = a;
+    f.n_splits = p.splits;
+    f.partial = part;
+    f.lse = lse;
+    hipError_t e = sa::launch_fwd_fewq(f, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "few-query forward launch");
+    sa::CombineArgs c{};
+    c.partial = part;
+    c.lse = lse;
+    c.out = a.out;
+    c.nq = a.nq;
+    c.o_rs = a.o_rs;
+    c.o_hs = a.o_hs;
+    c.heads = ctx->heads;
+    c.n_splits = runs;
+    c.out_f32 = a.out_f32;
+    e = sa::launch_combine(c, ctx->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "few-query merge launch");
+    return SA_OK;
+}
+
 sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *bytes) {
     g_err[0] = 0;
     if (!bytes) return fail(SA_ERR_NULL, "bytes is NULL");
@@ -375,6 +434,11 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
     sa_status st = check_context(ctx);
     if (st != SA_OK) return st;
     if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
+    const FewqPlan f = fewq_plan(ctx, nq);
+    if (f.splits) {
+        *bytes = f.bytes;
+        return SA_OK;
+    }
     const TailPlan p = tail_plan(ctx, nq);
     *bytes = p.units ? tail_bytes(p, ctx->head_dim) : 0;
     return SA_OK;
@@ -430,13 +494,14 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
     sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
                                     out_dtype, o_row_stride, o_head_stride, a);
     if (st != SA_OK || nq == 0) return st;
-    const TailPlan p = tail_plan(ctx, nq);
-    if (!p.units || !workspace) return forward_launch(ctx, a, stream);
-    const size_t need = tail_bytes(p, ctx->head_dim);
+    const FewqPlan f = fewq_plan(ctx, nq);
+    const TailPlan p = f.splits ? TailPlan{} : tail_plan(ctx, nq);
+    if ((!f.splits && !p.units) || !workspace) return forward_launch(ctx, a, stream);
+    const size_t need = f.splits ? f.bytes : tail_bytes(p, ctx->head_dim);
     if (workspace_bytes < need)
         return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    return tail_launch(ctx, a, p, workspace, stream);
+    return f.splits ? fewq_launch(ctx, a, f, workspace, stream) : tail_launch(ctx, a, p, workspace, stream);
 }
 
 // Device address of `scratch` per device, looked up once per device (with
@@ -473,9 +538,10 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
     sa_status st = forward_out_args(ctx, q, nq, q_row_stride, q_head_stride, q_rope, q_norm, softmax_scale, out,
                                     out_dtype, o_row_stride, o_head_stride, a);
     if (st != SA_OK || nq == 0) return st;
-    const TailPlan p = tail_plan(ctx, nq);
-    if (!p.units) return forward_launch(ctx, a, stream);
-    const size_t need = tail_bytes(p, ctx->head_dim);
+    const FewqPlan f = fewq_plan(ctx, nq);  // (never more than the scratch holds)
+    const TailPlan p = f.splits ? TailPlan{} : tail_plan(ctx, nq);
+    if (!f.splits && !p.units) return forward_launch(ctx, a, stream);
+    const size_t need = f.splits ? f.bytes : tail_bytes(p, ctx->head_dim);
     if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
         return fail(SA_ERR_CAPACITY, "this forward needs %zu bytes of scratch; sa_forward_noalloc holds %zu",
                     need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
@@ -483,8 +549,8 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
     st = scratch_address(&ws);
     if (st != SA_OK) return st;
     // Every word of the scratch a call reads is written earlier in the same
-    // call (the tail's pieces, then the merge), so nothing needs clearing.
-    return tail_launch(ctx, a, p, ws, stream);
+    // call (the pieces or runs, then the merge), so nothing needs clearing.
+    return f.splits ? fewq_launch(ctx, a, f, ws, stream) : tail_launch(ctx, a, p, ws, stream);
 }
 
 sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,

@@ -148,4 +148,14 @@ int fwd_bf16_rows_per_workgroup();  // query rows one bf16 forward workgroup own
 constexpr int kFwdF32RowsPerWorkgroup = 64;
 hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t stream);
 
+// --- few-query forward (bf16) ----------------------------------------------
+// For 1 <= nq <= kFewqMaxRows: a.n_splits workgroups per head of kFewqWaves
+// waves, each wave one of R = kFewqWaves * a.n_splits equal runs of key tiles
+// (split_first_tile(r, R, tiles)); run r's normalised output and natural
+// log-sum-exp go to a.partial [R][nq][heads][d] and a.lse [R][nq][heads]
+// (an empty run: zeros and -inf), merged by launch_combine with R splits.
+constexpr int kFewqWaves = 4;
+constexpr int kFewqMaxRows = 64;
+hipError_t launch_fwd_fewq(const FwdArgs &a, int head_dim, hipStream_t stream);
+
 }  // namespace sa

@@ -87,12 +87,13 @@ def oracle(ca, rows=None):
 
 def rows_per_workgroup():
     """Query rows per (head, query tile) unit of the bf16 forward, read off the
-    workspace the library asks for: n_cu / 2 heads of one query row over 16 key
-    tiles make one part-empty round of n_cu / 2 units, which the stream-K tail
-    spreads over every CU, with 2 * n_cu slots of rows * (head_dim + 1) floats."""
+    workspace the library asks for: n_cu / 2 heads of SA_FEW_QUERY_ROWS + 1
+    query rows (one more than the few-query path takes) over 16 key tiles make
+    one part-empty round of n_cu / 2 units, which the stream-K tail spreads over
+    every CU, with 2 * n_cu slots of rows * (head_dim + 1) floats."""
     import torch
     from streaming_video_diffusion_amd import binding as B
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     ctx = B.PackedContext(n_cu // 2, 128, torch.bfloat16, 1024, device="cuda")
     ctx.rows = 1024
-    return B.sa_forward_workspace_bytes(ctx, 1) // (2 * n_cu * 129 * 4)
+    return B.sa_forward_workspace_bytes(ctx, B.SA_FEW_QUERY_ROWS + 1) // (2 * n_cu * 129 * 4)

@@ -50,12 +50,12 @@ def test_header_constants_match_binding():
     assert ctypes.sizeof(B.Segment) == 96
     assert ctypes.sizeof(B.Context) == 48
     assert ctypes.sizeof(B.RmsNorm) == 16
-    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 5
+    assert int(re.search(r"#define SA_ABI_VERSION (\d+)", text).group(1)) == 6
     assert int(re.search(r"#define SA_MAX_POOL (\d+)", text).group(1)) == 8
 
 
 def test_version_and_status_strings(L):
-    assert L.sa_abi_version() == 5
+    assert L.sa_abi_version() == 6
     assert L.sa_status_string(0) == b"SA_OK"
     for name, val in ERR.items():
         assert L.sa_status_string(val) == f"SA_ERR_{name}".encode()
@@ -250,6 +250,13 @@ def test_noalloc_scratch_limit_declared():
     text = open(HEADER).read()
     m = re.search(r"#define SA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.SA_NOALLOC_SCRATCH_BYTES
+
+
+def test_header_limits_match_the_binding():
+    text = open(HEADER).read()
+    for name in ("SA_FEW_QUERY_ROWS", "SA_MAX_SPLITS"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name), name
 
 
 def test_forward_split_errors(L):

@@ -127,10 +127,11 @@ def test_tail_strided_output_view():
     assert bool((big[outside] == 7.0).all())
 
 
-def test_tail_one_query_row():
-    """150 heads of one query row: every unit is a single valid row (the rest
-    of its 384 are padding the merge must skip), all in the tail."""
-    w = I.custom("tail_one_row", 602, "bf16", 150, 128, [1700, 1300], 1, prompt_rows=11)
+def test_tail_few_query_rows():
+    """150 heads of SA_FEW_QUERY_ROWS + 1 query rows (one more than the
+    few-query path takes): every unit holds 65 valid rows (the rest of its 384
+    are padding the merge must skip), all in the tail."""
+    w = I.custom("tail_few_rows", 602, "bf16", 150, 128, [1700, 1300], B.SA_FEW_QUERY_ROWS + 1, prompt_rows=11)
     r, first, ntiles = plan(w.nq, w.heads, w.nk)
     assert (r, first) == (150, 0)
     ca, out = run(w)

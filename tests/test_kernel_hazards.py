@@ -40,6 +40,21 @@ def test_every_forward_instantiation_is_clean(build, tmp_path):
         assert scan(body) == [], name
 
 
+def test_every_few_query_instantiation_is_clean(tmp_path):
+    """The few-query kernel's products are inline assembly too (head_dim 64/128 x one/two query blocks)."""
+    src = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fewq.hip")
+    out = tmp_path / "fewq.s"
+    flags = [f for f in BLD.FLAGS if f not in ("-fPIC", "-shared")]
+    r = subprocess.run([BLD.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(out)], capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    ks = {n: b for n, b in kernels(out.read_text()).items() if "fewq_kernel" in n}
+    assert len(ks) == 4, sorted(ks)
+    for name, body in ks.items():
+        assert body.count("v_mfma_f32_32x32x16_bf16") >= 32, name
+        assert scan(body) == [], name
+
+
 MFMA = "v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]"
 
 
