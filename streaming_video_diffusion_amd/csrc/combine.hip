@@ -5,7 +5,8 @@
 // the exponential of its log-sum-exp of scores: an identity of the softmax,
 // used here to cut the keys of few-query problems into runs processed by
 // separate workgroups. For every (row, head): LSE* = max_s lse_s,
-// w_s = exp(lse_s - LSE*), out = sum_s w_s partial_s / sum_s w_s.
+// w_s = exp(lse_s - LSE*), out = sum_s w_s partial_s / sum_s w_s (LSE* taken
+// as the running max of a single pass, the sums rescaled as it grows).
 // D / 4 lanes per (row, head), 16 bytes each; memory-bound (reads n_splits
 // partial rows, writes one row). The same merge finishes the pieces of the
 // units a stream-K tail cut between workgroups.
@@ -41,18 +42,50 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int64_t row = rh / a.heads;
     const int head = (int)(rh - row * a.heads);
     const int64_t stride = a.nq * a.heads;  // between splits, in (row, head) units
+    // One pass over the splits, kB at a time (their loads issued together):
+    // mx is the largest log-sum-exp so far, and acc, wsum hold the sums
+    // weighted relative to it, rescaled whenever it grows. An empty split
+    // (lse -inf, zero output) weighs 0.
+    constexpr int kB = 8;
     float mx = -__builtin_inff();
-    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.lse[s * stride + rh]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-        const float wgt = expf(a.lse[s * stride + rh] - mx);
-        wsum += wgt;
-        const f32x4 p = *reinterpret_cast<const f32x4 *>(a.partial + (s * stride + rh) * D + c);
-        acc.x = __builtin_fmaf(wgt, p.x, acc.x);
-        acc.y = __builtin_fmaf(wgt, p.y, acc.y);
-        acc.z = __builtin_fmaf(wgt, p.z, acc.z);
-        acc.w = __builtin_fmaf(wgt, p.w, acc.w);
+    for (int s0 = 0; s0 < a.n_splits; s0 += kB) {
+        const int nb = a.n_splits - s0 < kB ? a.n_splits - s0 : kB;
+        float lv[kB];
+        f32x4 pv[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            if (i < nb) {
+                const int64_t at = (s0 + i) * stride + rh;
+                lv[i] = a.lse[at];
+                pv[i] = *reinterpret_cast<const f32x4 *>(a.partial + at * D + c);
+            } else {
+                lv[i] = -__builtin_inff();
+                pv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float mb = lv[0];
+#pragma unroll
+        for (int i = 1; i < kB; ++i) mb = fmaxf(mb, lv[i]);
+        if (mb > mx) {
+            const float sc = mx == -__builtin_inff() ? 0.f : expf(mx - mb);
+            acc.x *= sc;
+            acc.y *= sc;
+            acc.z *= sc;
+            acc.w *= sc;
+            wsum *= sc;
+            mx = mb;
+        }
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const float wgt = lv[i] == -__builtin_inff() ? 0.f : expf(lv[i] - mx);
+            wsum += wgt;
+            acc.x = __builtin_fmaf(wgt, pv[i].x, acc.x);
+            acc.y = __builtin_fmaf(wgt, pv[i].y, acc.y);
+            acc.z = __builtin_fmaf(wgt, pv[i].z, acc.z);
+            acc.w = __builtin_fmaf(wgt, pv[i].w, acc.w);
+        }
     }
     const float inv = 1.0f / wsum;
     const f32x4 r = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
