@@ -84,6 +84,9 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (3 times) and exit; "
                         "its FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
+    p.add_argument("--few-query-only", action="store_true",
+                   help="only time the 40 audio-only queries of the video+audio chunk (few-query path, "
+                        "split-KV, plain forward) and print them as one JSON line")
     return p.parse_args()
 
 
@@ -220,29 +223,38 @@ def other_workloads(steps, skip):
         res[w.name] = {"nq": w.nq, "nk": w.nk, "forward_ms": ms, "pack_tables_ms": pack,
                        "tflops": w.flops_per_call() / (ms * 1e-3) / 1e12}
         if w.name == "video_audio_1344x768":
-            q, qt = ca.q[w.nq - 40:], ca.q_table[w.nq - 40:]
-            out = torch.empty((40, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
-            part = torch.empty((32, 40, w.heads, w.head_dim), dtype=torch.float32, device="cuda:0")
-            lse = torch.empty((32, 40, w.heads), dtype=torch.float32, device="cuda:0")
-
-            def split():
-                B.sa_forward_split(ca.ctx, q, 32, qt, w.scale, partial=part, lse=lse, stream=stream)
-                B.sa_combine_splits(part, lse, out=out, stream=stream)
-
-            plain = _time(lambda: B.sa_forward(ca.ctx, q, qt, w.scale, out=out, stream=stream), stream, steps)
-            need = B.sa_forward_workspace_bytes(ca.ctx, 40)
-            ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
-            fewq = _time(lambda: B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws),
-                         stream, steps)
-            nbytes = w.nk * w.heads * w.head_dim * 2 * 2 + 2 * 40 * w.heads * w.head_dim * 2
-            res["audio_40q_over_52752kv"] = {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps),
-                                             "few_query_ms": fewq, "few_query_bytes": nbytes,
-                                             "few_query_tb_per_s": nbytes / (fewq * 1e-3) / 1e12,
-                                             "few_query_hbm_frac": nbytes / (fewq * 1e-3) / HBM_PEAK_BPS}
+            res["audio_40q_over_52752kv"] = audio_measure(ca, w, stream, steps)
         del ca
         torch.cuda.empty_cache()
     res["tier_stream_1344x768"] = tier_stream_measure(steps)
     return res
+
+
+def audio_measure(ca, w, stream, steps):
+    """The 40 audio-only queries of the video+audio chunk (packed in ``ca``)
+    over its 52752 keys: one plain forward, 32 key splits + merge, and the
+    few-query path (sa_forward_ws: one key run per wave + merge) with its
+    rate over the K/V, Q and output bytes."""
+    import torch
+    from streaming_video_diffusion_amd import binding as B
+    q, qt = ca.q[w.nq - 40:], ca.q_table[w.nq - 40:]
+    out = torch.empty((40, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
+    part = torch.empty((32, 40, w.heads, w.head_dim), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((32, 40, w.heads), dtype=torch.float32, device="cuda:0")
+
+    def split():
+        B.sa_forward_split(ca.ctx, q, 32, qt, w.scale, partial=part, lse=lse, stream=stream)
+        B.sa_combine_splits(part, lse, out=out, stream=stream)
+
+    plain = _time(lambda: B.sa_forward(ca.ctx, q, qt, w.scale, out=out, stream=stream), stream, steps)
+    need = B.sa_forward_workspace_bytes(ca.ctx, 40)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
+    fewq = _time(lambda: B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws), stream, steps)
+    nbytes = w.nk * w.heads * w.head_dim * 2 * 2 + 2 * 40 * w.heads * w.head_dim * 2
+    return {"plain_forward_ms": plain, "split32_plus_merge_ms": _time(split, stream, steps),
+            "few_query_ms": fewq, "few_query_bytes": nbytes,
+            "few_query_tb_per_s": nbytes / (fewq * 1e-3) / 1e12,
+            "few_query_hbm_frac": nbytes / (fewq * 1e-3) / HBM_PEAK_BPS}
 
 
 def tier_stream_measure(steps):
@@ -330,10 +342,27 @@ class SclkSampler:
                 "source": "pp_dpm_sclk (driver-reported current shader clock), sampled during the timed steps"}
 
 
+def few_query_only(steps):
+    """The audio-query measurement alone (for profiling the few-query kernel)."""
+    import torch
+    from streaming_video_diffusion_amd import inputs as I
+    from streaming_video_diffusion_amd.stream import ChunkAttention
+    stream = torch.cuda.current_stream()
+    w = I.video_audio_1344x768()
+    ca = ChunkAttention(w, device="cuda:0")
+    ca.pack_static(stream)
+    ca.step(stream)
+    res = audio_measure(ca, w, stream, steps)
+    print(json.dumps({"workload": "audio_40q_over_52752kv", "steps": steps, **res}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.few_query_only:
+        few_query_only(args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
