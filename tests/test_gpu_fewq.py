@@ -40,6 +40,28 @@ def test_workspace_bytes_of_the_few_query_plan():
     ctx = B.PackedContext(6, 128, torch.bfloat16, 1024)
     ctx.rows = 1000
     assert B.sa_forward_workspace_bytes(ctx, B.SA_FEW_QUERY_ROWS + 1) != fewq_bytes(64, 6, 128, 1000)
+    # A plan larger than the library's scratch (2048 heads x 64 rows: 4 runs x 64 x 2048 x 129 x 4 B =
+    # 270 MB) is not used: such a call sizes its workspace for the other paths.
+    assert 4 * 64 * 2048 * 129 * 4 > B.SA_NOALLOC_SCRATCH_BYTES
+    ctx = B.PackedContext(2048, 128, torch.bfloat16, 256)
+    ctx.rows = 256
+    assert fewq_bytes(64, 2048, 128, 256) == 0
+    assert B.sa_forward_workspace_bytes(ctx, 64) <= B.SA_NOALLOC_SCRATCH_BYTES
+
+
+def test_plan_larger_than_the_scratch_takes_the_other_paths():
+    """2048 heads of 64 rows over 256 keys: no few-query plan; sa_forward_ws and
+    sa_forward_noalloc still agree with the oracle."""
+    w = I.custom("fewq_too_big", 725, "bf16", 2048, 128, [200], 64, prompt_rows=56)
+    ca, out = run(w)
+    rows = np.array([0, 31, 32, 63])
+    heads = np.array([0, 1, 1023, 2047])
+    ref = oracle(ca, rows=rows)
+    rel, mx = assert_parity(out[rows][:, heads], ref[:, heads], "bf16", w.name)
+    note(f"  {w.name}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
+    got = B.sa_forward_noalloc(ca.ctx, ca.q, torch.empty_like(ca.out), ca.q_table, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ca.out)
 
 
 # (nq, head_dim, heads, out dtype, qk-norm): one and two 32-row query blocks,
