@@ -16,14 +16,16 @@
 //     scale*log2(e), one bf16 rounding), so each K/V byte is read from HBM
 //     once per call;
 //   * K and V^T operands go from global memory straight to registers (no
-//     other wave reads them, so no LDS): the next tile's K is requested once
-//     this tile's Q.K^T products have read theirs, its V^T once the P.V
-//     products have;
+//     other wave reads them, so no LDS), a tile in two 32-key halves: the
+//     next tile's K half is requested once this half's Q.K^T products have
+//     read theirs, its V^T half once the P.V products have;
 //   * S^T = K Q^T and O^T += V^T P^T (the main kernel's orientation), so one
-//     lane holds one query's scores and outputs; online softmax whose running
-//     max m (log2 units) is raised only when a tile's max exceeds it by more
-//     than 8, which keeps every P = 2^(s - m) at most 256 and the rescale of
-//     the accumulators off the common path;
+//     lane holds one query's scores and outputs. The softmax is the main
+//     kernel's: the anchor stays at 0 (P = 2^s, log2 units) in the main pass,
+//     which also tracks each row's exact max; a wave any of whose rows ends
+//     with a sum outside [2^-100, 2^100] or a non-finite output runs its key
+//     run again anchored at that max (rare), so the accumulators are never
+//     rescaled;
 //   * each wave stores its run's normalised float32 output and natural
 //     log-sum-exp (an empty run: zeros and -inf), and the split-KV merge
 //     (combine_kernel) forms the result.
