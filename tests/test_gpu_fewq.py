@@ -203,3 +203,37 @@ def test_audio_only_queries_full_size():
     rows = np.arange(w.nq - 40, w.nq)
     rel, mx = assert_parity(got.cpu().numpy().astype(np.float64), oracle(ca, rows=rows), "bf16", "audio rows")
     note(f"  audio rows: rel-L2 {rel:.3e} max-abs {mx:.3e}")
+
+
+@pytest.mark.parametrize("entry", ["noalloc", "ws"])
+def test_captured_and_replayed(entry):
+    """The few-query path captured into a HIP graph (after one eager call) and
+    replayed; each replay bitwise equal to the eager result, with an eager
+    few-query call of other size on the same scratch or workspace between."""
+    w = I.custom("fewq_graph", 726, "bf16", 40, 128, [2000, 1500], 40, prompt_rows=32)
+    ca, _ = run(w)
+    ws = torch.empty(B.sa_forward_workspace_bytes(ca.ctx, w.nq), dtype=torch.uint8, device="cuda")
+
+    def call(q, qt, out, stream=None):
+        if entry == "noalloc":
+            return B.sa_forward_noalloc(ca.ctx, q, out, qt, w.scale, stream=stream)
+        return B.sa_forward_ws(ca.ctx, q, qt, w.scale, out=out, stream=stream, workspace=ws)
+
+    eager = torch.empty_like(ca.out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(ca.q, ca.q_table, eager, stream=side)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ca.out)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(ca.q, ca.q_table, out, stream=side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        call(ca.q[:17], ca.q_table[:17], torch.empty_like(ca.out[:17]))  # eager work on the same scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
