@@ -387,7 +387,11 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
  *                                   over the run's keys (natural log, float32).
  * sa_combine_splits then yields exactly the sa_forward result: softmax over a
  * union of disjoint key sets is the LSE-weighted mean of the per-set softmax
- * attentions. Arguments as in sa_forward; partial is device float32
+ * attentions. A bf16 call of at most SA_FEW_QUERY_ROWS rows whose
+ * heads * n_splits runs number at least twice the device's compute units
+ * computes each run in one wave of the few-query kernel (see sa_forward_ws);
+ * others run the main forward kernel, one workgroup per run and query tile.
+ * Arguments as in sa_forward; partial is device float32
  * [n_splits][nq][heads][head_dim] (16-byte aligned), lse device float32
  * [n_splits][nq][heads]; 1 <= n_splits <= min(SA_MAX_SPLITS, T).
  * Errors: as sa_forward; SA_ERR_SHAPE for n_splits.

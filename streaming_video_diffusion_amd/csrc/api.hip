@@ -408,6 +408,7 @@ static sa_status fewq_launch(const sa_context *ctx, const sa::FwdArgs &a, const 
     float *lse = part + (size_t)runs * a.nq * ctx->heads * ctx->head_dim;
     sa::FwdArgs f = a;
     f.n_splits = p.splits;
+    f.fewq_runs = runs;
     f.partial = part;
     f.lse = lse;
     hipError_t e = sa::launch_fwd_fewq(f, ctx->head_dim, stream);
@@ -567,10 +568,25 @@ sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int
     if (nq == 0) return SA_OK;
     if (!partial || !lse) return fail(SA_ERR_NULL, "partial / lse is NULL");
     if (!aligned(partial, 16) || !aligned(lse, 4)) return fail(SA_ERR_ALIGN, "partial must be 16-byte aligned");
-    a.n_splits = n_splits;
     a.partial = partial;
     a.lse = lse;
     a.out_f32 = 1;
+    int dev = 0, n_cu = 0;
+    if (!SA_ROTATE_K_IN_FORWARD && ctx->dtype == SA_BF16 && nq <= sa::kFewqMaxRows && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        (int64_t)ctx->heads * n_splits >= 2 * (int64_t)n_cu) {
+        // Few query rows and enough runs to give every SIMD of the chip about
+        // two: the few-query kernel, one wave per split (its runs are the
+        // splits' key-tile ranges, its partial layout theirs). Fewer runs
+        // would leave most SIMDs idle; the forward kernel then does better
+        // (one workgroup per run).
+        a.n_splits = (n_splits + sa::kFewqWaves - 1) / sa::kFewqWaves;
+        a.fewq_runs = n_splits;
+        hipError_t e = sa::launch_fwd_fewq(a, ctx->head_dim, stream);
+        if (e != hipSuccess) return hip_fail(e, "few-query forward launch");
+        return SA_OK;
+    }
+    a.n_splits = n_splits;
     return forward_launch(ctx, a, stream);
 }
 

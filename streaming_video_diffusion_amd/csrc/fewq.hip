@@ -10,7 +10,8 @@
 // matrix cores bound the run, while the whole K/V stream is a fraction of a
 // millisecond of HBM time. Here every wave works on its own run of keys:
 //   * one workgroup of four waves per (head, split); wave w of split s owns
-//     run g = 4 s + w of G = 4 n_splits equal contiguous runs of 64-key tiles;
+//     run g = 4 s + w of G (at most 4 n_splits) equal contiguous runs of
+//     64-key tiles;
 //   * every wave holds all (at most 64) query rows of its head in registers,
 //     prepared as the main kernel prepares them (QK-norm, fp32 rotation,
 //     scale*log2(e), one bf16 rounding), so each K/V byte is read from HBM
@@ -158,8 +159,9 @@ __global__ __launch_bounds__(kFewqWaves * 64) void fewq_kernel(FwdArgs a) {
     const int hf = lane >> 5;
     const int head = blockIdx.x / a.n_splits;
     const int split = blockIdx.x - head * a.n_splits;
-    const int nrun = kFewqWaves * a.n_splits;
+    const int nrun = a.fewq_runs;
     const int run = split * kFewqWaves + w;
+    if (run >= nrun) return;  // (no LDS, no barriers: the other waves go on alone)
     const int ntiles = (int)((a.nk + BN - 1) / BN);
     const int nfull = (int)(a.nk / BN);  // tiles with no padding keys
     const int t0 = split_first_tile(run, nrun, ntiles);
@@ -331,8 +333,9 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_fewq(const FwdArgs &a, int head_dim, hipStream_t stream) {
-    if (a.nq < 1 || a.nq > kFewqMaxRows || a.n_splits < 1 || !a.partial || !a.lse ||
-        (int64_t)a.heads * a.n_splits > 0x7fffffff || a.k_table)
+    if (a.nq < 1 || a.nq > kFewqMaxRows || a.n_splits < 1 || a.fewq_runs < 1 ||
+        a.fewq_runs > kFewqWaves * a.n_splits || !a.partial || !a.lse || (int64_t)a.heads * a.n_splits > 0x7fffffff ||
+        a.k_table)
         return hipErrorInvalidValue;
     const bool two = a.nq > 32;
     if (head_dim == 128) return two ? launch_t<128, 2>(a, stream) : launch_t<128, 1>(a, stream);

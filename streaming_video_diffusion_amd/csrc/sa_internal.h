@@ -118,6 +118,8 @@ struct FwdArgs {
     int32_t tail_wgs;
     float *tail_part;
     float *tail_lse;
+    // Few-query kernel: key runs per head (its waves past the last run exit).
+    int32_t fewq_runs;
 };
 // Key tiles [first, end) of split s of n over ntiles tiles (balanced, non-empty when n <= ntiles).
 __host__ __device__ inline int split_first_tile(int s, int n, int ntiles) { return (int)((int64_t)s * ntiles / n); }
@@ -150,7 +152,8 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t stream);
 
 // --- few-query forward (bf16) ----------------------------------------------
 // For 1 <= nq <= kFewqMaxRows: a.n_splits workgroups per head of kFewqWaves
-// waves, each wave one of R = kFewqWaves * a.n_splits equal runs of key tiles
+// waves, wave w of workgroup s taking run r = kFewqWaves s + w of the
+// R = a.fewq_runs (at most kFewqWaves * a.n_splits) equal runs of key tiles
 // (split_first_tile(r, R, tiles)); run r's normalised output and natural
 // log-sum-exp go to a.partial [R][nq][heads][d] and a.lse [R][nq][heads]
 // (an empty run: zeros and -inf), merged by launch_combine with R splits.

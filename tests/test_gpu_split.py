@@ -94,6 +94,26 @@ def test_split_with_qknorm():
     check(packed(w), 6, "bf16")
 
 
+@pytest.mark.parametrize("n_splits", [1, 5, 29])
+def test_split_few_rows(n_splits):
+    """40 query rows (bf16) of 128 heads: 5 and 29 runs per head (at least
+    twice as many runs as a 256-CU part has CUs) take one wave of the few-query
+    kernel each, 1 run the forward kernel; 1828 keys = 29 tiles, ragged last,
+    so 29 runs hold one tile each."""
+    w = I.custom("split_few", 422, "bf16", 128, 128, [1200, 605], 40, prompt_rows=23)
+    assert w.nk == 1828 and w.nq <= B.SA_FEW_QUERY_ROWS
+    check(packed(w), n_splits, "bf16")
+
+
+def test_split_few_rows_d64_qknorm_and_second_pass():
+    w = dataclasses.replace(I.custom("split_few_d64", 423, "bf16", 96, 64, [700, 333], 17, prompt_rows=9),
+                            qk_norm="per_head")
+    check(packed(w), 6, "bf16")
+    w = I.custom("split_few_peaked", 424, "bf16", 128, 128, [150, 333], 40, rotary=False, prompt_rows=40,
+                 scale=float(np.float32(4.0 * math.log(2.0))))
+    check(packed(w), 4, "bf16")
+
+
 def test_audio_only_queries_full_size():
     """The 40 audio queries of the 1 s video+audio chunk (24232 q x 52752 kv), 32 key runs."""
     w = I.video_audio_1344x768()
