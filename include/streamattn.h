@@ -313,9 +313,10 @@ sa_status sa_forward(const sa_context *ctx, const void *q, int64_t nq, int64_t q
  * audio-only queries of a joint chunk: MiniMax-H3 deep-dive page, components
  * table and DiT paragraph) takes the few-query path instead: every wave of a
  * key-split kernel streams its own equal run of the head's key tiles for all
- * nq rows, S = n_cu / heads workgroups of four waves per head (at least 1, at
- * most a quarter of the key tiles), each run stored as its normalised float32
- * output and log-sum-exp and the runs merged as sa_combine_splits merges them.
+ * nq rows, R = 4 n_cu / heads runs per head (at least 1, at most the key
+ * tiles; four waves per workgroup, a workgroup's waves possibly of different
+ * heads), each run stored as its normalised float32 output and log-sum-exp
+ * and the runs merged as sa_combine_splits merges them.
  * It reads the packed K/V once and fills the chip however few the rows are.
  * workspace: device, 16-byte aligned, at least sa_forward_workspace_bytes()
  *            bytes for this context and nq on the current device; NULL (or a
@@ -357,9 +358,9 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
  * serves) bytes of workspace sa_forward_ws uses for this
  * context and nq on the current device (0 when it would run as sa_forward):
  * 2 * n_cu * 384 * (head_dim + 1) * 4 when the stream-K tail is used (101.4 MB
- * at head_dim 128 on 256 CUs); 4 S * nq * heads * (head_dim + 1) * 4 on the
- * few-query path (S workgroups per head as above; 9.9 MB for 40 rows of 40
- * heads at head_dim 128 on 256 CUs). A few-query plan that would need more than
+ * at head_dim 128 on 256 CUs); R * nq * heads * (head_dim + 1) * 4 on the
+ * few-query path (R runs per head as above; 20.6 MB for 40 rows of 40 heads
+ * at head_dim 128 on 256 CUs). A few-query plan that would need more than
  * SA_NOALLOC_SCRATCH_BYTES is not used (such a forward takes the other paths).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, and the context checks of sa_forward.
  */

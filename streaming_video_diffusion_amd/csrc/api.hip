@@ -370,14 +370,14 @@ static size_t tail_bytes(const TailPlan &p, int head_dim) {
 
 // Few-query plan of the bf16 forward: for 1 <= nq <= kFewqMaxRows every wave
 // of the few-query kernel streams its own run of key tiles for all the
-// queries of a head, S workgroups (4 S runs) per head, S = n_cu / heads so
-// that one round fills the chip (at least 1, and at most a quarter of the key
-// tiles so that no run is empty). The runs' partial outputs take
-// 4 S * nq * heads * (head_dim + 1) float32 values of workspace; a plan that
-// would need more than SA_NOALLOC_SCRATCH_BYTES is not used, so that
-// sa_forward_noalloc and sa_forward_ws run the same launches.
+// queries of a head, R runs per head, R = 4 n_cu / heads so that one round of
+// waves fills the chip (at least 1, at most the key tiles so that no run is
+// empty). The runs' partial outputs take R * nq * heads * (head_dim + 1)
+// float32 values of workspace; a plan that would need more than
+// SA_NOALLOC_SCRATCH_BYTES is not used, so that sa_forward_noalloc and
+// sa_forward_ws run the same launches.
 struct FewqPlan {
-    int splits = 0;  // workgroups per head (0: not used)
+    int runs = 0;  // runs per head (0: not used)
     size_t bytes = 0;
 };
 static FewqPlan fewq_plan(const sa_context *ctx, int64_t nq) {
@@ -387,27 +387,25 @@ static FewqPlan fewq_plan(const sa_context *ctx, int64_t nq) {
     if (hipGetDevice(&dev) != hipSuccess) return p;
     if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0) return p;
     const int64_t ntiles = (ctx->rows + SA_ROW_ALIGN - 1) / SA_ROW_ALIGN;
-    int64_t s = n_cu / ctx->heads;
-    if (s > ntiles / sa::kFewqWaves) s = ntiles / sa::kFewqWaves;
-    if (s < 1) s = 1;
-    const size_t bytes =
-        (size_t)sa::kFewqWaves * s * (size_t)nq * ctx->heads * (size_t)(ctx->head_dim + 1) * sizeof(float);
+    int64_t r = (int64_t)sa::kFewqWaves * n_cu / ctx->heads;
+    if (r > ntiles) r = ntiles;
+    if (r < 1) r = 1;
+    const size_t bytes = (size_t)r * (size_t)nq * ctx->heads * (size_t)(ctx->head_dim + 1) * sizeof(float);
     if (bytes > (size_t)SA_NOALLOC_SCRATCH_BYTES) return p;
-    p.splits = (int)s;
+    p.runs = (int)r;
     p.bytes = bytes;
     return p;
 }
 
 // The launches of a few-query forward (a: validated arguments, p: a plan with
-// splits > 0, workspace: device memory of at least p.bytes): every run's
+// runs > 0, workspace: device memory of at least p.bytes): every run's
 // partial output and log-sum-exp, then their merge into out.
 static sa_status fewq_launch(const sa_context *ctx, const sa::FwdArgs &a, const FewqPlan &p, void *workspace,
                              hipStream_t stream) {
-    const int32_t runs = sa::kFewqWaves * p.splits;
+    const int32_t runs = p.runs;
     float *part = static_cast<float *>(workspace);
     float *lse = part + (size_t)runs * a.nq * ctx->heads * ctx->head_dim;
     sa::FwdArgs f = a;
-    f.n_splits = p.splits;
     f.fewq_runs = runs;
     f.partial = part;
     f.lse = lse;
@@ -436,7 +434,7 @@ sa_status sa_forward_workspace_bytes(const sa_context *ctx, int64_t nq, size_t *
     if (st != SA_OK) return st;
     if (nq < 0) return fail(SA_ERR_SHAPE, "nq %lld < 0", (long long)nq);
     const FewqPlan f = fewq_plan(ctx, nq);
-    if (f.splits) {
+    if (f.runs) {
         *bytes = f.bytes;
         return SA_OK;
     }
@@ -496,13 +494,13 @@ sa_status sa_forward_ws(const sa_context *ctx, const void *q, int64_t nq, int64_
                                     out_dtype, o_row_stride, o_head_stride, a);
     if (st != SA_OK || nq == 0) return st;
     const FewqPlan f = fewq_plan(ctx, nq);
-    const TailPlan p = f.splits ? TailPlan{} : tail_plan(ctx, nq);
-    if ((!f.splits && !p.units) || !workspace) return forward_launch(ctx, a, stream);
-    const size_t need = f.splits ? f.bytes : tail_bytes(p, ctx->head_dim);
+    const TailPlan p = f.runs ? TailPlan{} : tail_plan(ctx, nq);
+    if ((!f.runs && !p.units) || !workspace) return forward_launch(ctx, a, stream);
+    const size_t need = f.runs ? f.bytes : tail_bytes(p, ctx->head_dim);
     if (workspace_bytes < need)
         return fail(SA_ERR_CAPACITY, "workspace_bytes %zu below the %zu this forward needs", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    return f.splits ? fewq_launch(ctx, a, f, workspace, stream) : tail_launch(ctx, a, p, workspace, stream);
+    return f.runs ? fewq_launch(ctx, a, f, workspace, stream) : tail_launch(ctx, a, p, workspace, stream);
 }
 
 // Device address of `scratch` per device, looked up once per device (with
@@ -540,9 +538,9 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
                                     out_dtype, o_row_stride, o_head_stride, a);
     if (st != SA_OK || nq == 0) return st;
     const FewqPlan f = fewq_plan(ctx, nq);  // (never more than the scratch holds)
-    const TailPlan p = f.splits ? TailPlan{} : tail_plan(ctx, nq);
-    if (!f.splits && !p.units) return forward_launch(ctx, a, stream);
-    const size_t need = f.splits ? f.bytes : tail_bytes(p, ctx->head_dim);
+    const TailPlan p = f.runs ? TailPlan{} : tail_plan(ctx, nq);
+    if (!f.runs && !p.units) return forward_launch(ctx, a, stream);
+    const size_t need = f.runs ? f.bytes : tail_bytes(p, ctx->head_dim);
     if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
         return fail(SA_ERR_CAPACITY, "this forward needs %zu bytes of scratch; sa_forward_noalloc holds %zu",
                     need, (size_t)SA_NOALLOC_SCRATCH_BYTES);
@@ -551,7 +549,7 @@ sa_status sa_forward_noalloc(const sa_context *ctx, const void *q, int64_t nq, i
     if (st != SA_OK) return st;
     // Every word of the scratch a call reads is written earlier in the same
     // call (the pieces or runs, then the merge), so nothing needs clearing.
-    return f.splits ? fewq_launch(ctx, a, f, ws, stream) : tail_launch(ctx, a, p, ws, stream);
+    return f.runs ? fewq_launch(ctx, a, f, ws, stream) : tail_launch(ctx, a, p, ws, stream);
 }
 
 sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int64_t q_row_stride,
@@ -580,7 +578,6 @@ sa_status sa_forward_split(const sa_context *ctx, const void *q, int64_t nq, int
         // splits' key-tile ranges, its partial layout theirs). Fewer runs
         // would leave most SIMDs idle; the forward kernel then does better
         // (one workgroup per run).
-        a.n_splits = (n_splits + sa::kFewqWaves - 1) / sa::kFewqWaves;
         a.fewq_runs = n_splits;
         hipError_t e = sa::launch_fwd_fewq(a, ctx->head_dim, stream);
         if (e != hipSuccess) return hip_fail(e, "few-query forward launch");

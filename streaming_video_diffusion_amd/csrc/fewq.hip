@@ -9,9 +9,9 @@
 // main kernel's 384-row workgroup keeps one wave of four busy and that wave's
 // matrix cores bound the run, while the whole K/V stream is a fraction of a
 // millisecond of HBM time. Here every wave works on its own run of keys:
-//   * one workgroup of four waves per (head, split); wave w of split s owns
-//     run g = 4 s + w of G (at most 4 n_splits) equal contiguous runs of
-//     64-key tiles;
+//   * every wave of the grid owns one of R equal contiguous runs of one
+//     head's 64-key tiles (wave g: head g / R, run g % R), four waves per
+//     workgroup;
 //   * every wave holds all (at most 64) query rows of its head in registers,
 //     prepared as the main kernel prepares them (QK-norm, fp32 rotation,
 //     scale*log2(e), one bf16 rounding), so each K/V byte is read from HBM
@@ -157,11 +157,13 @@ __global__ __launch_bounds__(kFewqWaves * 64) void fewq_kernel(FwdArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
     const int hf = lane >> 5;
-    const int head = blockIdx.x / a.n_splits;
-    const int split = blockIdx.x - head * a.n_splits;
+    // Wave g of the grid takes run g % R of head g / R (R runs per head): the
+    // waves share nothing, so a workgroup's four may serve different heads.
     const int nrun = a.fewq_runs;
-    const int run = split * kFewqWaves + w;
-    if (run >= nrun) return;  // (no LDS, no barriers: the other waves go on alone)
+    const int64_t g = (int64_t)blockIdx.x * kFewqWaves + w;
+    const int head = (int)(g / nrun);
+    if (head >= a.heads) return;  // the grid's last waves (no LDS, no barriers: the others go on alone)
+    const int run = (int)(g - (int64_t)head * nrun);
     const int ntiles = (int)((a.nk + BN - 1) / BN);
     const int nfull = (int)(a.nk / BN);  // tiles with no padding keys
     const int t0 = split_first_tile(run, nrun, ntiles);
@@ -325,17 +327,17 @@ __global__ __launch_bounds__(kFewqWaves * 64) void fewq_kernel(FwdArgs a) {
 
 template <int D, int QB>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((fewq_kernel<D, QB>), dim3((unsigned)((int64_t)a.heads * a.n_splits)), dim3(kFewqWaves * 64), 0,
-                       stream, a);
+    const int64_t waves = (int64_t)a.heads * a.fewq_runs;
+    hipLaunchKernelGGL((fewq_kernel<D, QB>), dim3((unsigned)((waves + kFewqWaves - 1) / kFewqWaves)),
+                       dim3(kFewqWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fewq(const FwdArgs &a, int head_dim, hipStream_t stream) {
-    if (a.nq < 1 || a.nq > kFewqMaxRows || a.n_splits < 1 || a.fewq_runs < 1 ||
-        a.fewq_runs > kFewqWaves * a.n_splits || !a.partial || !a.lse || (int64_t)a.heads * a.n_splits > 0x7fffffff ||
-        a.k_table)
+    if (a.nq < 1 || a.nq > kFewqMaxRows || a.fewq_runs < 1 || !a.partial || !a.lse ||
+        (int64_t)a.heads * a.fewq_runs > 0x7fffffffLL || a.k_table)
         return hipErrorInvalidValue;
     const bool two = a.nq > 32;
     if (head_dim == 128) return two ? launch_t<128, 2>(a, stream) : launch_t<128, 1>(a, stream);

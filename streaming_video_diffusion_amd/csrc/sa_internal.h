@@ -118,7 +118,7 @@ struct FwdArgs {
     int32_t tail_wgs;
     float *tail_part;
     float *tail_lse;
-    // Few-query kernel: key runs per head (its waves past the last run exit).
+    // Few-query kernel: key runs per head, one wave each.
     int32_t fewq_runs;
 };
 // Key tiles [first, end) of split s of n over ntiles tiles (balanced, non-empty when n <= ntiles).
@@ -151,12 +151,12 @@ constexpr int kFwdF32RowsPerWorkgroup = 64;
 hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t stream);
 
 // --- few-query forward (bf16) ----------------------------------------------
-// For 1 <= nq <= kFewqMaxRows: a.n_splits workgroups per head of kFewqWaves
-// waves, wave w of workgroup s taking run r = kFewqWaves s + w of the
-// R = a.fewq_runs (at most kFewqWaves * a.n_splits) equal runs of key tiles
-// (split_first_tile(r, R, tiles)); run r's normalised output and natural
-// log-sum-exp go to a.partial [R][nq][heads][d] and a.lse [R][nq][heads]
-// (an empty run: zeros and -inf), merged by launch_combine with R splits.
+// For 1 <= nq <= kFewqMaxRows: one wave per (head, run) of R = a.fewq_runs
+// equal runs of each head's key tiles (run r: split_first_tile(r, R, tiles)
+// onwards), kFewqWaves waves per workgroup; run r's normalised output and
+// natural log-sum-exp go to a.partial [R][nq][heads][d] and a.lse
+// [R][nq][heads] (an empty run: zeros and -inf), merged by launch_combine
+// with R splits. (a.n_splits is not used.)
 constexpr int kFewqWaves = 4;
 constexpr int kFewqMaxRows = 64;
 hipError_t launch_fwd_fewq(const FwdArgs &a, int head_dim, hipStream_t stream);

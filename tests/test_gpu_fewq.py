@@ -23,8 +23,8 @@ def fewq_bytes(nq, heads, head_dim, nk):
     if not 1 <= nq <= B.SA_FEW_QUERY_ROWS:
         return 0
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    s = max(1, min(n_cu // heads, math.ceil(nk / 64) // 4))
-    n = 4 * s * nq * heads * (head_dim + 1) * 4
+    runs = max(1, min(4 * n_cu // heads, math.ceil(nk / 64)))
+    n = runs * nq * heads * (head_dim + 1) * 4
     return n if n <= B.SA_NOALLOC_SCRATCH_BYTES else 0
 
 
@@ -40,22 +40,24 @@ def test_workspace_bytes_of_the_few_query_plan():
     ctx = B.PackedContext(6, 128, torch.bfloat16, 1024)
     ctx.rows = 1000
     assert B.sa_forward_workspace_bytes(ctx, B.SA_FEW_QUERY_ROWS + 1) != fewq_bytes(64, 6, 128, 1000)
-    # A plan larger than the library's scratch (2048 heads x 64 rows: 4 runs x 64 x 2048 x 129 x 4 B =
-    # 270 MB) is not used: such a call sizes its workspace for the other paths.
-    assert 4 * 64 * 2048 * 129 * 4 > B.SA_NOALLOC_SCRATCH_BYTES
-    ctx = B.PackedContext(2048, 128, torch.bfloat16, 256)
-    ctx.rows = 256
-    assert fewq_bytes(64, 2048, 128, 256) == 0
+    # A plan larger than the library's scratch (4096 heads x 64 rows: one run each,
+    # 64 x 4096 x 129 x 4 B = 135.3 MB) is not used: such a call sizes its
+    # workspace for the other paths.
+    assert 64 * 4096 * 129 * 4 > B.SA_NOALLOC_SCRATCH_BYTES
+    ctx = B.PackedContext(4096, 128, torch.bfloat16, 64)
+    ctx.rows = 64
+    assert fewq_bytes(64, 4096, 128, 64) == 0
     assert B.sa_forward_workspace_bytes(ctx, 64) <= B.SA_NOALLOC_SCRATCH_BYTES
 
 
 def test_plan_larger_than_the_scratch_takes_the_other_paths():
-    """2048 heads of 64 rows over 256 keys: no few-query plan; sa_forward_ws and
+    """4096 heads of 64 rows over 64 keys: no few-query plan; sa_forward_ws and
     sa_forward_noalloc still agree with the oracle."""
-    w = I.custom("fewq_too_big", 725, "bf16", 2048, 128, [200], 64, prompt_rows=56)
+    w = I.custom("fewq_too_big", 725, "bf16", 4096, 128, [24], 64, prompt_rows=40)
+    assert w.nk == 64
     ca, out = run(w)
     rows = np.array([0, 31, 32, 63])
-    heads = np.array([0, 1, 1023, 2047])
+    heads = np.array([0, 1, 2047, 4095])
     ref = oracle(ca, rows=rows)
     rel, mx = assert_parity(out[rows][:, heads], ref[:, heads], "bf16", w.name)
     note(f"  {w.name}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
@@ -95,9 +97,9 @@ def test_few_query_rows_against_the_oracle(nq, d, heads, out_dtype, qkn):
     assert d_rel < 5e-3, d_rel
 
 
-def test_runs_with_no_key_tiles():
-    """100 keys are two tiles: the head's four runs hold one, one, zero and zero
-    tiles (rows of the empty runs carry -inf log-sum-exps into the merge)."""
+def test_two_key_tiles():
+    """100 keys are two tiles: as many runs as tiles (one each), the second
+    one holding the padded tile."""
     w = I.custom("fewq_empty_runs", 720, "bf16", 3, 128, [77], 40, prompt_rows=23)
     assert w.nk == 100
     ca, out = run(w)
