@@ -48,6 +48,7 @@
 #include "sa_internal.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace sa {
 
@@ -120,13 +121,13 @@ struct Tile {
         for (int ii = 0; ii < KINSTR / NW; ++ii) {
             const int i = w * (KINSTR / NW) + ii;
             const int r = i * KROWS_PER_INSTR + lane / (KROW / 16);
-            pl.k[ii] = (uint32_t)(r * KROW + kswz(r, lane % (KROW / 16)) * 16);
+            pl.k[ii] = (uint32_t)(r * KROW + kswz(r, lane % (KROW / 16)) * 16 - ii * 1024);
         }
 #pragma unroll
         for (int ii = 0; ii < VINSTR / NW; ++ii) {
             const int i = w * (VINSTR / NW) + ii;
             const int r = i * VROWS_PER_INSTR + lane / 8;
-            pl.v[ii] = (uint32_t)(r * cap * 2 + swz128(r, lane % 8) * 16);
+            pl.v[ii] = (uint32_t)(r * cap * 2 + swz128(r, lane % 8) * 16 - ii * 1024);
         }
         return pl;
     }
@@ -141,14 +142,20 @@ struct Tile {
     // read-ahead of the operand reads.)
     __device__ static __forceinline__ void issue(unsigned char *buf, const Plan &pl, __amdgpu_buffer_rsrc_t kr,
                                                  __amdgpu_buffer_rsrc_t vr, uint32_t k0, int w) {
-#pragma unroll
-        for (int ii = 0; ii < KINSTR / NW; ++ii)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(buf + (w * (KINSTR / NW) + ii) * 1024), 16,
-                                                     (int)pl.k[ii], (int)(k0 * KROW), 0, 0);
-#pragma unroll
-        for (int ii = 0; ii < VINSTR / NW; ++ii)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(buf + KBYTES + (w * (VINSTR / NW) + ii) * 1024),
-                                                     16, (int)pl.v[ii], (int)(k0 * 2), 0, 0);
+        issue_seq(buf + w * (KINSTR / NW) * 1024, pl.k, kr, (int)(k0 * KROW),
+                  std::make_integer_sequence<int, KINSTR / NW>());
+        issue_seq(buf + KBYTES + w * (VINSTR / NW) * 1024, pl.v, vr, (int)(k0 * 2),
+                  std::make_integer_sequence<int, VINSTR / NW>());
+    }
+    // Loads ii = 0.. of one wave's share write 1 KiB each to consecutive LDS
+    // kilobytes from one LDS base: the step is the instruction's immediate
+    // offset, which moves the LDS and the global address alike (the lane
+    // offsets of the plan have it subtracted), so the base is set once.
+    template <int N, int... II>
+    __device__ static __forceinline__ void issue_seq(unsigned char *dst, const uint32_t (&off)[N],
+                                                     __amdgpu_buffer_rsrc_t rs, int soff,
+                                                     std::integer_sequence<int, II...>) {
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, (int)off[II], soff, II * 1024, 0), ...);
     }
 };
 
@@ -382,6 +389,12 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
         return (uint32_t)(buf_of(kt) - smem) + A0 + (uint32_t)(half * 32 * T::KROW);
     };
     auto vtile = [&](int kt) __attribute__((always_inline)) { return (uint32_t)(buf_of(kt) - smem) + B0; };
+    // The same from a buffer's byte offset (the main loop carries the offsets
+    // of tiles kt, kt + 1 and kt + 2 from one tile to the next).
+    auto kunit_at = [&](uint32_t bo, int half) __attribute__((always_inline)) {
+        return bo + A0 + (uint32_t)(half * 32 * T::KROW);
+    };
+    auto vtile_at = [&](uint32_t bo) __attribute__((always_inline)) { return bo + B0; };
     auto kread = [&](uint32_t kb, int j) __attribute__((always_inline)) { return lds_read16(kb ^ (uint32_t)(32 * j)); };
     // V^T operand read r = g * DT + c of the unit (half) of a tile
     auto vread = [&](uint32_t vb, int half, int r) __attribute__((always_inline)) {
@@ -474,16 +487,13 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
         constexpr int NS = (QK ? NQK : 0) + NPV;
         constexpr int NV = QB * 16;
         constexpr int PER = NV / NS > 1 ? NV / NS : 1;  // exponentials per slot
-        float ls[QB];
-#pragma unroll
-        for (int b = 0; b < QB; ++b) ls[b] = 0.f;
         auto exp_v = [&](int v) __attribute__((always_inline)) {
             sr[v >> 4][v & 15] = __builtin_amdgcn_exp2f(sr[v >> 4][v & 15]);
         };
         auto sum_pack_v = [&](int v) __attribute__((always_inline)) {
             const int b = v >> 4, i = v & 15;
-            ls[b] += sr[b][i];
-            asm volatile("" :: "v"(ls[b]));
+            l[b] += sr[b][i];
+            asm volatile("" :: "v"(l[b]));
             if (i & 1) {
                 bf16x2 pp;
                 pp.x = (bf16)sr[b][i - 1];
@@ -549,8 +559,6 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
             for (int v = (NS - EOFF) * PER; v < NV; ++v) exp_v(v);
 #pragma unroll
             for (int v = (NS - EOFF - 2) * PER; v < NV; ++v) sum_pack_v(v);
-#pragma unroll
-            for (int b = 0; b < QB; ++b) l[b] += ls[b];
 #pragma unroll
             for (int b = 0; b < QB; ++b) asm volatile("" :: "v"(l[b]), "v"(pw[b][0]), "v"(pw[b][1]));
         }
@@ -629,17 +637,25 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, const int qt, const 
         // Stage i = 2 kt' + h: P.V of unit i (tile kt, half h), Q.K^T of unit
         // i + 2 (tile kt + 1, half h), exponentials of unit i + 1. S of unit u
         // lives in sA when u is even, sB when odd; P likewise in pA / pB.
+        // Inside the loop tile kt is never the context's last (kt + 1 < ntiles
+        // <= ntiles_all), so only unit 0 of tile kt + 1 can need the mask.
         int kt = t_begin;
+        uint32_t bo0 = (uint32_t)(buf_of(kt) - smem), bo1 = (uint32_t)(buf_of(kt + 1) - smem),
+                 bo2 = (uint32_t)(buf_of(kt + 2) - smem);
         for (; kt + 1 < ntiles; ++kt) {
             if constexpr (ROTK) rotate_k(kt + 1);
-            issue(kt + NSTAGE - 1);
-            mask(sB, kt, 1);
-            stage(bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), bconst<true>(), kunit(kt + 1, 0),
-                  kunit(kt + 1, 1), vtile(kt), 0, vtile(kt), 1, sA, sB, pA, pB, kpre, vpre);
+            if (kt + NSTAGE - 1 < ntiles)
+                T::issue(smem + bo2, T::plan(a.cap, wu, lane), krs, vrs, (uint32_t)((kt + NSTAGE - 1) * BN), wu);
+            stage(bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), bconst<true>(), kunit_at(bo1, 0),
+                  kunit_at(bo1, 1), vtile_at(bo0), 0, vtile_at(bo0), 1, sA, sB, pA, pB, kpre, vpre);
             mask(sA, kt + 1, 0);
-            stage(bconst<true>(), bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), kunit(kt + 1, 1),
-                  0u, vtile(kt), 1, vtile(kt + 1), 0, sB, sA, pB, pA, kpre, vpre);
+            stage(bconst<true>(), bconst<true>(), bconst<true>(), bconst<false>(), bconst<true>(), kunit_at(bo1, 1),
+                  0u, vtile_at(bo0), 1, vtile_at(bo1), 0, sB, sA, pB, pA, kpre, vpre);
             end_tile();
+            const uint32_t bt = bo0;
+            bo0 = bo1;
+            bo1 = bo2;
+            bo2 = bt;
         }
         // last tile: P.V of its two units, exponentials of its second unit
         if constexpr (ROTK) rotate_k(kt + 1);
