@@ -36,9 +36,9 @@ FWD_SOURCE = os.path.join(ROOT, "streaming_video_diffusion_amd", "csrc", "fwd_bf
 # written). Valid only for the forward source these counters were taken on
 # (None: not taken on the current source).
 TRAFFIC = {
-    "source_sha256": "0c85cf8ecbb13ea63afd3d961ac755b9536fba70eccbceae808bd330c9d08b7b",
-    "fetch_kib": 466622.1,
-    "write_kib": 120964.2,
+    "source_sha256": "ff3bef451d868e6afd1faa1a076543104ce4c16cbbd3659416af7220bff10d4d",
+    "fetch_kib": 466617.6,
+    "write_kib": 120963.7,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
