@@ -294,15 +294,23 @@ def tier_stream_measure(steps):
 
 class SclkSampler:
     """Samples the shader clock the driver reports (the line marked '*' in
-    the DRM device's pp_dpm_sclk) every ``period`` seconds on a host thread,
-    while the GPU runs the timed steps. Reports nothing where the file is
-    absent or unreadable."""
+    the DRM device's pp_dpm_sclk) and, where the device's hwmon exposes it,
+    the board power it reports (power1_average, else power1_input, in uW, and
+    its cap power1_cap) every ``period`` seconds on a host thread, while the
+    GPU runs the timed steps. Reports nothing where the files are absent or
+    unreadable."""
 
     def __init__(self, period=0.01):
         import glob
         import threading
         self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-        self.period, self.samples = period, []
+        self.power_paths = []
+        for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+            for name in ("power1_average", "power1_input"):
+                if os.path.exists(os.path.join(d, name)):
+                    self.power_paths.append((os.path.join(d, name), os.path.join(d, "power1_cap")))
+                    break
+        self.period, self.samples, self.power = period, [], []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -318,28 +326,47 @@ class SclkSampler:
                 continue
         return None
 
+    @staticmethod
+    def _read_uw(path):
+        try:
+            with open(path) as f:
+                return float(f.read().strip())
+        except (OSError, ValueError):
+            return None
+
     def _run(self):
         while not self._stop.wait(self.period):
             v = self._read()
             if v is not None:
                 self.samples.append(v)
+            for path, _ in self.power_paths[:1]:
+                uw = self._read_uw(path)
+                if uw is not None:
+                    self.power.append(uw * 1e-6)
 
     def __enter__(self):
-        if self.paths:
+        if self.paths or self.power_paths:
             self._thread.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        if self.paths:
+        if self.paths or self.power_paths:
             self._thread.join()
 
     def summary(self):
         if not self.samples:
             return None
         v = sorted(self.samples)
-        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
-                "source": "pp_dpm_sclk (driver-reported current shader clock), sampled during the timed steps"}
+        out = {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+               "source": "pp_dpm_sclk (driver-reported current shader clock), sampled during the timed steps"}
+        if self.power:
+            pw = sorted(self.power)
+            cap = self._read_uw(self.power_paths[0][1])
+            out["board_power_w"] = {"median": pw[len(pw) // 2], "max": pw[-1], "samples": len(pw),
+                                    "cap": cap * 1e-6 if cap else None,
+                                    "source": os.path.basename(self.power_paths[0][0]) + " (hwmon, driver-reported)"}
+        return out
 
 
 def few_query_only(steps):

@@ -55,7 +55,7 @@ __device__ __forceinline__ float partner(float x) {
 // with two wait states of its own (a VALU write of one of its operands may
 // come right before it), and every read of a product's result by other
 // instructions goes through a drain below, which takes the registers it
-// protects as operands (a 16-pass product needs 19 wait states before other
+// protects as operands (an 8-pass product needs 11 wait states before other
 // instructions touch its result; four s_nop 7 give 32).
 
 // O^T += V^T P^T (a = V^T, b = P^T).
@@ -148,7 +148,8 @@ __device__ __forceinline__ void load_q(const FwdArgs &a, int head, int64_t row, 
     }
 }
 
-// a.n_splits workgroups per head, QB blocks of 32 query rows (nq <= 32 QB).
+// a.fewq_runs waves per head, kFewqWaves waves per workgroup, QB blocks of 32
+// query rows (nq <= 32 QB).
 template <int D, int QB>
 __global__ __launch_bounds__(kFewqWaves * 64) void fewq_kernel(FwdArgs a) {
     constexpr int DC = D / 16;  // k-steps of Q.K^T
